@@ -1,0 +1,82 @@
+"""8-bit scaled ("Sage") decode attention in float64 (oracle; test infrastructure).
+
+Formula followed ([FlashInfer-Sage], code §1, the README "Sage attention"
+block), for one attention row r and key position c:
+
+    S[r][c] = sfQ[blkQ(r)] · sfK[blkK(c)] · (Q8 · K8ᵀ)[r][c]
+    P       = row softmax of S, stored as the E4M3 value of 448·p
+    O[r][d] = sfV[d] · (Σ_c P8[r][c] · V8[c][d]) / (448 · l[r])   (+ v_mean[d])
+
+Scale conventions ([FlashInfer-Sage], code §1 and §4): the caller quantises
+and supplies the scales; Q and K scales enter before the row max and the
+exponential; V scales apply per channel after the sum; scale values are not
+checked.
+
+Readings where the pages are silent or at odds:
+
+* The 8-bit formula carries no 1/sqrt(d) although the attention definition
+  ([FA-vs-PA], FlashAttention §1) does: ``sm_scale`` multiplies the
+  dequantised S (``sm_scale=1`` gives the formula literally).
+* Dividing by 448·l only makes sense if P8 holds the *unnormalised*
+  exp(S - m), so l is the float sum of the unquantised p = exp(S - m), and
+  m is the row max of S.  This oracle takes m as the final row max.
+* blkK(c) = c // k_block on the logical position c in the request; sfK is
+  [B, Hkv, nblk]; decode has one query row per request so sfQ is [B, Hq];
+  sfV and v_mean are [B, Hkv, d].
+* E4M3 is the OCP E4M3FN variant (largest finite value 448).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+from .e4m3 import e4m3_decode, e4m3_encode
+
+
+def sage_decode(q8, k8_pool, v8_pool, req_to_token, seq_lens, sfq, sfk, sfv,
+                k_block: int, sm_scale: Optional[float] = None, v_mean=None,
+                quantize_p: bool = True, req_pool_indices=None):
+    """One query row per request. q8: [B, Hq, d] uint8 codes; pools [slots, Hkv, d].
+
+    Returns (o [B, Hq, d] float64, lse [B, Hq] float64) with lse = m + ln l in
+    the (scaled) S domain.  ``quantize_p=False`` keeps 448·p unrounded.
+    """
+    q8 = np.asarray(q8)
+    B, Hq, d = q8.shape
+    Hkv = k8_pool.shape[1]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    lse = np.full((B, Hq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        row = b if req_pool_indices is None else int(req_pool_indices[b])
+        L = int(seq_lens[b])
+        if L == 0:
+            if v_mean is not None:
+                out[b] = np.repeat(np.asarray(v_mean[b], np.float64), G, axis=0)
+            continue
+        slots = np.asarray(req_to_token[row, :L], dtype=np.int64)
+        K = e4m3_decode(np.asarray(k8_pool)[slots])  # [L, Hkv, d] exact
+        V = e4m3_decode(np.asarray(v8_pool)[slots])
+        blk = np.arange(L) // k_block
+        for h in range(Hq):
+            g = h // G
+            qv = e4m3_decode(q8[b, h])  # [d]
+            dots = K[:, g, :] @ qv  # exact in fp64 (products of 4-bit significands)
+            S = sm_scale * float(sfq[b, h]) * np.asarray(sfk[b, g, blk], np.float64) * dots
+            m = S.max()
+            p = np.exp(S - m)
+            l = p.sum()
+            P8 = 448.0 * p
+            if quantize_p:
+                P8 = e4m3_decode(e4m3_encode(P8))
+            acc = P8 @ V[:, g, :]  # [d]
+            o = np.asarray(sfv[b, g], np.float64) * acc / (448.0 * l)
+            if v_mean is not None:
+                o = o + np.asarray(v_mean[b, g], np.float64)
+            out[b, h] = o
+            lse[b, h] = m + math.log(l)
+    return out, lse

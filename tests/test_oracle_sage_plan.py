@@ -1,0 +1,166 @@
+"""Pins of the 8-bit (Sage) oracle, the scheduling re-derivation, the KV store
+and the score-memory helper."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import Spec, make_host_batch, make_layout
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FP8 = Spec("f8", "decode", 3, 4, 2, 32, 4, (3, 70), 1, dtype="fp8", k_block=16)
+
+
+def _sage(hb, **kw):
+    lay = hb.layout
+    return oracle.sage_decode(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens,
+                              hb.sfq, hb.sfk, hb.sfv, hb.layout.spec.k_block, **kw)
+
+
+def test_sage_unit_scales_unquantised_p_reduce_to_plain_attention():
+    hb = make_host_batch(FP8, 0)
+    lay = hb.layout
+    hb.sfq[:] = 1.0
+    hb.sfk[:] = 1.0
+    hb.sfv[:] = 1.0
+    o, lse = _sage(hb, quantize_p=False)
+    q = oracle.e4m3_decode(hb.q_codes)
+    k = oracle.e4m3_decode(hb.k_codes)
+    v = oracle.e4m3_decode(hb.v_codes)
+    o2, lse2 = oracle.paged_attention(q, k, v, lay.req_to_token, lay.seq_lens, lay.cu_seqlens_q)
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-12, atol=1e-12)
+
+
+def test_sage_scales_enter_before_softmax():
+    """sfQ·sfK multiply the scores: folding them into sm_scale per request is the same."""
+    hb = make_host_batch(FP8, 1)
+    hb.sfk[:] = 1.25
+    hb.sfq[:] = 0.5
+    o, lse = _sage(hb)
+    hb.sfk[:] = 1.0
+    hb.sfq[:] = 1.0
+    o2, lse2 = _sage(hb, sm_scale=0.625 / math.sqrt(FP8.head_dim))
+    np.testing.assert_allclose(o, o2, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-14, atol=1e-14)
+
+
+def test_sage_constant_scores_give_scaled_mean():
+    hb = make_host_batch(FP8, 2)
+    lay = hb.layout
+    hb.q_codes[:] = 0  # q = 0: every score is 0, p = 1, P8 = 448 exactly
+    o, lse = _sage(hb)
+    G = FP8.num_q_heads // FP8.num_kv_heads
+    for b in range(FP8.batch):
+        L = int(lay.seq_lens[b])
+        V = oracle.e4m3_decode(hb.v_codes[lay.req_to_token[b, :L]])
+        for h in range(FP8.num_q_heads):
+            g = h // G
+            np.testing.assert_allclose(o[b, h], hb.sfv[b, g] * V[:, g].mean(axis=0), rtol=1e-14, atol=1e-14)
+            assert abs(lse[b, h] - math.log(L)) < 1e-13
+
+
+def test_sage_power_of_two_sfv_is_exact():
+    hb = make_host_batch(FP8, 3)
+    o1, _ = _sage(hb)
+    hb.sfv *= 4.0
+    o2, _ = _sage(hb)
+    assert np.array_equal(o2, 4.0 * o1)
+
+
+def test_sage_two_key_hand_example():
+    with open(os.path.join(GOLDEN, "sage_two_keys.json")) as f:
+        g = json.load(f)
+    q8 = oracle.e4m3_encode(np.array(g["q"]))[None, None, :]
+    k8 = oracle.e4m3_encode(np.array(g["k"]))[:, None, :]
+    v8 = oracle.e4m3_encode(np.array(g["v"]))[:, None, :]
+    assert np.array_equal(oracle.e4m3_decode(k8)[:, 0], np.array(g["k"]))
+    rtt = np.array([[0, 1]])
+    sfv = np.array(g["sfv"])[None, None, :]
+    o, lse = oracle.sage_decode(q8, k8, v8, rtt, [2], np.ones((1, 1)), np.ones((1, 1, 1)), sfv,
+                                k_block=64, sm_scale=math.log(2))
+    np.testing.assert_allclose(o[0, 0], g["expected_o"], rtol=1e-15, atol=1e-15)
+    assert abs(lse[0, 0] - math.log(1.5)) < 1e-15
+
+
+def test_sage_p_quantisation_changes_little():
+    hb = make_host_batch(FP8, 4)
+    o_q, _ = _sage(hb)
+    o_f, _ = _sage(hb, quantize_p=False)
+    rel = np.linalg.norm(o_q - o_f) / np.linalg.norm(o_f)
+    assert 0 < rel < 5e-2
+
+
+# ---------------------------------------------------------------- plan
+@pytest.mark.parametrize("kv_chunk", [0, 32, 96])
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_plan_invariants(seed, kv_chunk):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    max_kv = int(rng.integers(1, 5000))
+    L = rng.integers(0, max_kv + 1, size=B)
+    L[rng.integers(0, B)] = max_kv + 77  # beyond the bound: must be clamped
+    Hkv, G = 8, int(rng.choice([1, 4, 8, 20]))
+    plan = oracle.plan_decode(L, Hkv, G, max_kv, kv_chunk=kv_chunk, split_target=int(rng.integers(1, 9000)))
+    items = plan["items"]
+    assert len(items) <= plan["capacity"]
+    Lc = np.minimum(L, max_kv)
+    parts = []
+    for b in range(B):
+        mine = items[items[:, 0] == b]
+        assert len(mine) == plan["splits"][b] >= 1
+        assert mine[0, 1] == 0 and mine[-1, 2] == Lc[b]
+        assert np.all(mine[1:, 1] == mine[:-1, 2])  # contiguous, in order
+        assert np.all(mine[:, 1] % oracle.DECODE_TILE == 0)
+        if Lc[b] > 0:
+            assert np.all(mine[:, 2] > mine[:, 1])  # no empty split
+        if len(mine) == 1:
+            assert mine[0, 3] == -1
+        else:
+            parts += list(mine[:, 3])
+        if kv_chunk:
+            assert np.all(mine[:, 2] - mine[:, 1] <= kv_chunk)
+    assert sorted(parts) == sorted(set(parts))
+    assert np.all(np.diff(items[:, 0]) >= 0)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_extend_plan_invariants(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 20))
+    n = rng.integers(0, 300, size=B)
+    p = rng.integers(0, 300, size=B)
+    L = n + p
+    cu = np.concatenate([[0], np.cumsum(n)])
+    G = int(rng.choice([1, 2, 4, 8, 3]))
+    plan = oracle.plan_extend(L, cu, G, int(L.max()) if B else 1, int(cu[-1]))
+    bt = plan["block_tokens"]
+    items = plan["items"]
+    assert len(items) <= plan["capacity"]
+    assert np.all(np.diff(items[:, 2]) <= 0)  # longest causal range first
+    for b in range(B):
+        mine = sorted(items[items[:, 0] == b][:, 1])
+        assert mine == list(range(-(-int(n[b]) // bt)))
+        for it in items[items[:, 0] == b]:
+            assert it[2] == p[b] + min((it[1] + 1) * bt, n[b])
+
+
+def test_kv_store_round_trip():
+    lay, rng = make_layout(Spec("k", "extend", 3, 2, 2, 8, 4, (0, 9), (1, 5)), 0)
+    pool = rng.standard_normal((lay.pool_slots, 2, 8))
+    new = rng.standard_normal((lay.total_q, 2, 8))
+    out = oracle.kv_store(pool, new, lay.new_slots)
+    assert np.array_equal(out[lay.new_slots], new)
+    untouched = np.setdiff1d(np.arange(lay.pool_slots), lay.new_slots)
+    assert np.array_equal(out[untouched], pool[untouched])
+
+
+def test_score_memory_figures_from_the_flashattention_page():
+    with open(os.path.join(GOLDEN, "fa_memory.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        got = oracle.score_matrix_bytes(c["seq_len"], c["elem_bytes"], c["heads"], c["batch"])
+        assert got == c["approx_bytes"]

@@ -1,0 +1,292 @@
+"""Seeded synthetic workloads for paged-KV attention.
+
+This module only draws inputs: request lengths, a shuffled page pool, the
+two-level page table and N(0, 1) values (rounded to the storage type by a
+plain cast).  It holds none of the attention arithmetic, so the CPU oracle
+and the HIP library can both be fed from it without sharing any method code.
+
+Shapes and distributions follow the workloads the library is measured on:
+
+=====================  =====================================================
+name                   description
+=====================  =====================================================
+``tiny_decode``        B=2, 4 q / 2 kv heads, d=64, page 1, cached {37,100},
+                       one new token each; fp32 N(0,1); the page table is a
+                       random permutation of a 256-slot pool
+``tiny_extend``        as above with {5,12} new tokens
+``decode_bf16``        B=64, 32 q / 8 kv heads, d=128, page 16, cached
+                       lengths U[512,4096]; pool = 2x the pages needed
+``extend_bf16``        16 requests, 32/8 heads, d=128, page 16, prefix
+                       U[0,2048] cached, U[128,2048] new tokens
+``long_decode_bf16``   B=8, 64/8 heads, d=128, page 64, cached U[32768,131072]
+``decode_fp8``         B=64, 32/8 heads, d=128, page 16, cached U[1024,8192];
+                       E4M3 codes of N(0,1)/scale with per-64-token sfK,
+                       per-(b,h) sfQ and per-channel sfV drawn from U[0.5,2]
+=====================  =====================================================
+
+Every decode workload appends one new token per request: the drawn value is
+the cached length and the attended length is ``cached + 1`` (the new token's
+K/V row is written by ``kv_store`` before attention reads it).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+LenSpec = Union[int, Tuple[int, int], Sequence[int]]
+
+
+@dataclass(frozen=True)
+class Spec:
+    """Shape of one synthetic batch.
+
+    ``prefix`` / ``new``: an int (same for all requests), a ``(lo, hi)`` tuple
+    (uniform integers, inclusive) or a list with one value per request.
+    ``pool``: ``"2x"`` for a shuffled pool with twice the pages needed, or an
+    int giving the total number of slots (the page table is then a random
+    permutation of that pool's pages).
+    """
+
+    name: str
+    mode: str  # "decode" or "extend"
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    prefix: LenSpec
+    new: LenSpec
+    dtype: str = "bf16"  # "fp32" (host-only tiny case), "bf16" or "fp8"
+    pool: Union[str, int] = "2x"
+    k_block: int = 64  # fp8: tokens per sfK block
+    q_block: int = 1  # fp8: q rows per sfQ block
+    scale_range: Tuple[float, float] = (0.5, 2.0)
+
+
+SPECS = {
+    "tiny_decode": Spec("tiny_decode", "decode", 2, 4, 2, 64, 1, [37, 100], 1,
+                        dtype="fp32", pool=256),
+    "tiny_extend": Spec("tiny_extend", "extend", 2, 4, 2, 64, 1, [37, 100], [5, 12],
+                        dtype="fp32", pool=256),
+    "decode_bf16": Spec("decode_bf16", "decode", 64, 32, 8, 128, 16, (512, 4096), 1),
+    "extend_bf16": Spec("extend_bf16", "extend", 16, 32, 8, 128, 16, (0, 2048), (128, 2048)),
+    "long_decode_bf16": Spec("long_decode_bf16", "decode", 8, 64, 8, 128, 64,
+                             (32768, 131072), 1),
+    "decode_fp8": Spec("decode_fp8", "decode", 64, 32, 8, 128, 16, (1024, 8192), 1,
+                       dtype="fp8", k_block=64, q_block=1),
+}
+
+# Index used to derive the seed of each named workload (1000 + index).
+SPEC_INDEX = {"tiny_decode": 1, "tiny_extend": 1, "decode_bf16": 2, "extend_bf16": 3,
+              "long_decode_bf16": 4, "decode_fp8": 5}
+
+
+def seed_sequence(spec: Spec, seed: int) -> list:
+    base = 1000 + SPEC_INDEX.get(spec.name, 9)
+    return [base, int(seed)]
+
+
+@dataclass
+class Layout:
+    """Integer structure of a batch: lengths and the two-level page table."""
+
+    spec: Spec
+    prefix_lens: np.ndarray  # int32 [B]   cached tokens before this step
+    new_lens: np.ndarray  # int32 [B]   tokens appended this step
+    seq_lens: np.ndarray  # int32 [B]   attended length = prefix + new
+    cu_seqlens_q: np.ndarray  # int32 [B+1] prefix sums of new_lens
+    req_to_token: np.ndarray  # int32 [B, stride]; -1 past seq_len
+    pool_slots: int  # rows in each per-layer K/V pool
+    new_slots: np.ndarray  # int32 [T] slot of each new token, request-major
+    slot_owner: np.ndarray  # int32 [pool_slots] request owning a slot, -1 if free
+    slot_pos: np.ndarray  # int32 [pool_slots] position of a slot in its request
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def max_kv_len(self) -> int:
+        return int(self.seq_lens.max()) if len(self.seq_lens) else 0
+
+
+def _draw(rng: np.random.Generator, spec_val: LenSpec, batch: int) -> np.ndarray:
+    if isinstance(spec_val, (int, np.integer)):
+        return np.full(batch, int(spec_val), dtype=np.int64)
+    if isinstance(spec_val, tuple):
+        lo, hi = spec_val
+        return rng.integers(lo, hi + 1, size=batch, dtype=np.int64)
+    arr = np.asarray(spec_val, dtype=np.int64)
+    assert arr.shape == (batch,), (arr.shape, batch)
+    return arr
+
+
+def make_layout(spec: Spec, seed: int = 0, rng: Optional[np.random.Generator] = None,
+                stride: Optional[int] = None) -> Tuple[Layout, np.random.Generator]:
+    """Draw lengths, then the page permutation, then build ``req_to_token``.
+
+    Positions j and j+1 of a request that fall in one page get consecutive
+    slots (slot = page * page_size + j % page_size).
+    """
+    if rng is None:
+        rng = np.random.default_rng(seed_sequence(spec, seed))
+    B, P = spec.batch, spec.page_size
+    prefix = _draw(rng, spec.prefix, B)
+    new = _draw(rng, spec.new, B)
+    if spec.mode == "decode":
+        assert np.all(new == 1), "decode appends exactly one token per request"
+    seq = prefix + new
+    pages_per_req = (seq + P - 1) // P
+    pages_needed = int(pages_per_req.sum())
+    if spec.pool == "2x":
+        num_pages = max(2 * pages_needed, 1)
+    else:
+        assert int(spec.pool) % P == 0
+        num_pages = int(spec.pool) // P
+        assert num_pages >= pages_needed, "pool too small for the drawn lengths"
+    perm = rng.permutation(num_pages)
+    max_len = int(seq.max()) if B else 0
+    if stride is None:
+        stride = max(max_len, 1)
+    assert stride >= max_len
+    rtt = np.full((B, stride), -1, dtype=np.int64)
+    slot_owner = np.full(num_pages * P, -1, dtype=np.int32)
+    slot_pos = np.full(num_pages * P, -1, dtype=np.int32)
+    nxt = 0
+    for b in range(B):
+        L = int(seq[b])
+        npg = int(pages_per_req[b])
+        pages = perm[nxt:nxt + npg]
+        nxt += npg
+        j = np.arange(L)
+        slots = pages[j // P] * P + (j % P)
+        rtt[b, :L] = slots
+        slot_owner[slots] = b
+        slot_pos[slots] = j
+    cu = np.zeros(B + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(new)
+    new_slots = np.concatenate(
+        [rtt[b, prefix[b]:seq[b]] for b in range(B)]) if B else np.zeros(0, np.int64)
+    lay = Layout(spec=spec, prefix_lens=prefix.astype(np.int32), new_lens=new.astype(np.int32),
+                 seq_lens=seq.astype(np.int32), cu_seqlens_q=cu.astype(np.int32),
+                 req_to_token=rtt.astype(np.int32), pool_slots=num_pages * P,
+                 new_slots=new_slots.astype(np.int32), slot_owner=slot_owner, slot_pos=slot_pos)
+    return lay, rng
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even) by a cast."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """OCP E4M3 (``float8_e4m3fn``) byte codes of float32 values, by a torch cast."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@dataclass
+class HostBatch:
+    """Layout plus host values (float32 arrays; bf16-exact when dtype is bf16).
+
+    ``k_pool``/``v_pool`` hold every referenced row *including* the new tokens
+    (the state after ``kv_store``); ``k_new``/``v_new`` are those new rows, in
+    ``new_slots`` order.  Unreferenced rows are NaN when ``poison`` was set.
+    fp8 batches carry E4M3 codes (uint8) in ``*_codes`` and the scales.
+    """
+
+    layout: Layout
+    q: np.ndarray  # [T, Hq, d]
+    k_pool: np.ndarray  # [slots, Hkv, d]
+    v_pool: np.ndarray
+    k_new: np.ndarray  # [T, Hkv, d]
+    v_new: np.ndarray
+    q_codes: Optional[np.ndarray] = None  # fp8 only, uint8
+    k_codes: Optional[np.ndarray] = None
+    v_codes: Optional[np.ndarray] = None
+    k_new_codes: Optional[np.ndarray] = None
+    v_new_codes: Optional[np.ndarray] = None
+    sfq: Optional[np.ndarray] = None  # [B, Hq] float32 (decode: one q block)
+    sfk: Optional[np.ndarray] = None  # [B, Hkv, nblk] float32
+    sfv: Optional[np.ndarray] = None  # [B, Hkv, d] float32
+
+
+def make_host_batch(spec: Spec, seed: int = 0, poison: bool = True,
+                    stride: Optional[int] = None) -> HostBatch:
+    """Draw a complete batch on the host (small and medium sizes).
+
+    Draw order: lengths, page permutation, Q, K pool, V pool, then scales.
+    """
+    lay, rng = make_layout(spec, seed, stride=stride)
+    T, Hq, Hkv, d = lay.total_q, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    S = lay.pool_slots
+    q = rng.standard_normal((T, Hq, d), dtype=np.float32)
+    k = rng.standard_normal((S, Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((S, Hkv, d), dtype=np.float32)
+    used = lay.slot_owner >= 0
+    if spec.dtype == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    hb = HostBatch(layout=lay, q=q, k_pool=k, v_pool=v, k_new=None, v_new=None)
+    if spec.dtype == "fp8":
+        B = spec.batch
+        lo, hi = spec.scale_range
+        nblk = max((lay.max_kv_len + spec.k_block - 1) // spec.k_block, 1)
+        sfq = rng.uniform(lo, hi, size=(B, Hq)).astype(np.float32)
+        sfk = rng.uniform(lo, hi, size=(B, Hkv, nblk)).astype(np.float32)
+        sfv = rng.uniform(lo, hi, size=(B, Hkv, d)).astype(np.float32)
+        # q rows of request b: decode has exactly one row per request
+        req_of_row = np.repeat(np.arange(B), lay.new_lens)
+        q_codes = e4m3_codes(q / sfq[req_of_row][:, :, None])
+        owner = np.where(used, lay.slot_owner, 0)
+        blk = np.where(used, lay.slot_pos, 0) // spec.k_block
+        ks = sfk[owner, :, blk]  # [S, Hkv]
+        vs = sfv[owner]  # [S, Hkv, d]
+        k_codes = e4m3_codes(k / ks[:, :, None])
+        v_codes = e4m3_codes(v / vs)
+        k_codes[~used] = 0x7F  # E4M3 NaN in unreferenced rows
+        v_codes[~used] = 0x7F
+        hb.q_codes, hb.k_codes, hb.v_codes = q_codes, k_codes, v_codes
+        hb.sfq, hb.sfk, hb.sfv = sfq, sfk, sfv
+        hb.k_new_codes = k_codes[lay.new_slots].copy()
+        hb.v_new_codes = v_codes[lay.new_slots].copy()
+    if poison:
+        k[~used] = np.nan
+        v[~used] = np.nan
+    hb.k_new = k[lay.new_slots].copy()
+    hb.v_new = v[lay.new_slots].copy()
+    return hb
+
+
+def pool_before_store(pool: np.ndarray, new_slots: np.ndarray, fill=np.nan) -> np.ndarray:
+    """Copy of a pool whose new-token rows are overwritten with ``fill``."""
+    out = pool.copy()
+    out[new_slots] = fill
+    return out
+
+
+def permute_pages(layout: Layout, rng: np.random.Generator) -> Tuple[Layout, np.ndarray]:
+    """Relabel the physical pages of a layout by a random permutation.
+
+    Returns the new layout and ``slot_map`` with ``new_slot = slot_map[old_slot]``;
+    moving every pool row ``r`` to ``slot_map[r]`` keeps the logical contents.
+    """
+    P = layout.spec.page_size
+    num_pages = layout.pool_slots // P
+    page_perm = rng.permutation(num_pages)
+    old = np.arange(layout.pool_slots)
+    slot_map = (page_perm[old // P] * P + old % P).astype(np.int64)
+    rtt = layout.req_to_token.astype(np.int64)
+    rtt_new = np.where(rtt >= 0, slot_map[np.maximum(rtt, 0)], -1).astype(np.int32)
+    owner = np.full_like(layout.slot_owner, -1)
+    pos = np.full_like(layout.slot_pos, -1)
+    owner[slot_map] = layout.slot_owner
+    pos[slot_map] = layout.slot_pos
+    new = replace(layout, req_to_token=rtt_new,
+                  new_slots=slot_map[layout.new_slots].astype(np.int32),
+                  slot_owner=owner, slot_pos=pos)
+    return new, slot_map
