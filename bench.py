@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A *step* is one pass of the hot path over one synthetic batch: the
+once-per-batch plan, then for each of ``--layers`` layers (each with its own
+K/V pools, so the 256 MB last-level cache cannot serve a layer from the
+previous one) the store of the step's new K/V rows and the attention call.
+
+The headline workload is the bf16 decode batch (B=64, 32 q / 8 kv heads,
+d=128, page 16, cached lengths U[512,4096]); ``value`` is its KV-read
+throughput: K+V bytes attended per step / step time.  The extend (prefill),
+long-context decode and 8-bit decode workloads are reported in
+``secondary`` with their own roofline figures.
+
+Prints ONE JSON line.  Inputs are resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode KV-read GB/s (% of HBM peak); extend TFLOP/s (% of MFMA peak)"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "flashattention_paged_kv_amd", "csrc")
+
+KERNEL_SOURCES = {
+    "decode_bf16": ["decode_bf16.hip", "device_common.h"],
+    "long_decode_bf16": ["decode_bf16.hip", "device_common.h"],
+    "decode_fp8": ["decode_fp8.hip", "device_common.h"],
+    "extend_bf16": ["extend_bf16.hip", "device_common.h"],
+}
+
+
+def source_hash(workload: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[workload]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters(workload: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None when
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != source_hash(workload):
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- workloads
+class DecodeRunner:
+    def __init__(self, name, layers, torch, pkv, workloads):
+        self.torch, self.pkv = torch, pkv
+        spec = workloads.SPECS[name]
+        self.spec = spec
+        self.fp8 = spec.dtype == "fp8"
+        self.db = workloads.make_device_batch(spec, seed=0, layers=layers)
+        lay = self.db.layout
+        self.layers = layers
+        kw = dict(kv_dtype=pkv.PKV_FP8_E4M3, q_block=spec.q_block, k_block=spec.k_block) if self.fp8 else {}
+        self.params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                                 max_kv_len=lay.req_to_token.shape[1], **kw)
+        ws_bytes, sc_bytes = pkv.workspace_size(self.params, pkv.PKV_DECODE, spec.batch)
+        self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        self.scratch = torch.empty(max(sc_bytes, 16), dtype=torch.uint8, device="cuda")
+        self.out = [torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.bfloat16, device="cuda")
+                    for _ in range(layers)]
+        self.lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+        esize = 1 if self.fp8 else 2
+        tokens = int(lay.seq_lens.astype("int64").sum())
+        self.kv_bytes_per_layer = tokens * spec.num_kv_heads * spec.head_dim * 2 * esize
+        self.work_per_step = self.kv_bytes_per_layer * layers
+
+    def step(self, events=None):
+        pkv, db = self.pkv, self.db
+        plan = pkv.plan_metadata(self.params, pkv.PKV_DECODE, db.seq_lens, workspace=self.ws)
+        for l in range(self.layers):
+            pkv.kv_store(self.params, db.k_pools[l], db.v_pools[l], db.k_new[l], db.v_new[l], db.new_slots)
+            if events is not None:
+                events.append(self.torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+            pkv.attn_decode(self.params, db.q, db.k_pools[l], db.v_pools[l], db.req_to_token, db.seq_lens, plan,
+                            scratch=self.scratch, out=self.out[l], lse=self.lse,
+                            sfq=db.sfq, sfk=db.sfk, sfv=db.sfv)
+            if events is not None:
+                events.append(self.torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+
+    def describe(self):
+        s = self.spec
+        lo, hi = s.prefix
+        return {"workload": s.name, "batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
+                "head_dim": s.head_dim, "page_size": s.page_size, "cached_len": f"U[{lo},{hi}] + 1 new token",
+                "kv_dtype": "fp8_e4m3" if self.fp8 else "bf16", "layers_per_step": self.layers,
+                "kv_bytes_per_layer": self.kv_bytes_per_layer}
+
+    def roofline(self, avg_launch_s, workload):
+        achieved = self.kv_bytes_per_layer / avg_launch_s / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_from_counters(workload),
+                "kernel": "decode_fp8_kernel + merge" if self.fp8 else "decode_bf16_kernel + decode_merge_kernel",
+                "algorithmic_bytes_per_launch": self.kv_bytes_per_layer,
+                "avg_launch_us": round(avg_launch_s * 1e6, 2)}
+
+    def cpu_baseline(self, budget_s, oracle):
+        """The fp64 oracle on layer 0 of the same batch, request by request until the budget is spent."""
+        import numpy as np
+        torch, db, spec = self.torch, self.db, self.spec
+        lay = db.layout
+        if self.fp8:
+            q = db.q.cpu().numpy()
+            kp = db.k_pools[0].cpu().numpy()
+            vp = db.v_pools[0].cpu().numpy()
+            sfq, sfk, sfv = db.sfq.cpu().numpy(), db.sfk.cpu().numpy(), db.sfv.cpu().numpy()
+        else:
+            q = db.q.float().cpu().numpy()
+            kp = db.k_pools[0].float().cpu().numpy()
+            vp = db.v_pools[0].float().cpu().numpy()
+        done_bytes, n = 0, 0
+        t0 = time.perf_counter()
+        for b in range(spec.batch):
+            rtt = lay.req_to_token[b:b + 1]
+            L = lay.seq_lens[b:b + 1]
+            if self.fp8:
+                oracle.sage_decode(q[b:b + 1], kp, vp, rtt, L, sfq[b:b + 1], sfk[b:b + 1], sfv[b:b + 1],
+                                   k_block=spec.k_block)
+            else:
+                oracle.paged_attention(q[b:b + 1], kp, vp, rtt, L, [0, 1])
+            done_bytes += int(L[0]) * spec.num_kv_heads * spec.head_dim * 2 * (1 if self.fp8 else 2)
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "seconds": round(dt, 2),
+                "sample": f"layer 0, requests 0..{n - 1} of {spec.batch} ({spec.name}), all {spec.num_q_heads} heads"}
+
+
+class ExtendRunner:
+    def __init__(self, name, layers, torch, pkv, workloads):
+        self.torch, self.pkv = torch, pkv
+        spec = workloads.SPECS[name]
+        self.spec = spec
+        self.db = workloads.make_device_batch(spec, seed=0, layers=layers)
+        lay = self.db.layout
+        self.layers = layers
+        self.params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                                 max_kv_len=lay.req_to_token.shape[1])
+        self.total_q = lay.total_q
+        ws_bytes, _ = pkv.workspace_size(self.params, pkv.PKV_EXTEND, spec.batch, self.total_q)
+        self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        self.out = [torch.empty((self.total_q, spec.num_q_heads, spec.head_dim), dtype=torch.bfloat16, device="cuda")
+                    for _ in range(layers)]
+        self.lse = torch.empty((self.total_q, spec.num_q_heads), dtype=torch.float32, device="cuda")
+        n = lay.new_lens.astype("int64")
+        p = lay.prefix_lens.astype("int64")
+        pairs = int((n * p + n * (n + 1) // 2).sum())  # unmasked (query, key) pairs per head
+        self.flops_per_layer = 4 * spec.head_dim * spec.num_q_heads * pairs
+        self.work_per_step = self.flops_per_layer * layers
+
+    def step(self, events=None):
+        pkv, db = self.pkv, self.db
+        plan = pkv.plan_metadata(self.params, pkv.PKV_EXTEND, db.seq_lens, db.cu_seqlens_q, total_q=self.total_q,
+                                 workspace=self.ws)
+        for l in range(self.layers):
+            pkv.kv_store(self.params, db.k_pools[l], db.v_pools[l], db.k_new[l], db.v_new[l], db.new_slots)
+            if events is not None:
+                events.append(self.torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+            pkv.attn_extend(self.params, db.q, db.k_pools[l], db.v_pools[l], db.req_to_token, db.seq_lens,
+                            db.cu_seqlens_q, plan, out=self.out[l], lse=self.lse)
+            if events is not None:
+                events.append(self.torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+
+    def describe(self):
+        s = self.spec
+        return {"workload": s.name, "batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
+                "head_dim": s.head_dim, "page_size": s.page_size, "prefix_len": f"U{list(s.prefix)}",
+                "new_len": f"U{list(s.new)}", "total_q": self.total_q, "layers_per_step": self.layers,
+                "flops_per_layer": self.flops_per_layer}
+
+    def roofline(self, avg_launch_s, workload):
+        achieved = self.flops_per_layer / avg_launch_s / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_counters(workload),
+                "kernel": "extend_bf16_kernel", "algorithmic_flops_per_launch": self.flops_per_layer,
+                "avg_launch_us": round(avg_launch_s * 1e6, 2)}
+
+
+RUNNERS = {"decode_bf16": DecodeRunner, "long_decode_bf16": DecodeRunner, "decode_fp8": DecodeRunner,
+           "extend_bf16": ExtendRunner}
+UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "decode_fp8": "GB/s", "extend_bf16": "TFLOP/s"}
+DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "decode_fp8": 4, "extend_bf16": 4}
+
+
+def measure(name, steps, warmup, layers, torch, pkv, workloads):
+    runner = RUNNERS[name](name, layers or DEFAULT_LAYERS[name], torch, pkv, workloads)
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    events = []
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        runner.step(events)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(0, len(events), 2)]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    scale = 1e9 if UNITS[name] == "GB/s" else 1e12
+    value = runner.work_per_step / (ms / 1e3) / scale
+    return runner, ms, value, runner.roofline(avg_launch_s, name)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_bf16", choices=sorted(RUNNERS))
+    ap.add_argument("--layers", type=int, default=0, help="layers (distinct K/V pools) per step")
+    ap.add_argument("--secondary", default="extend_bf16,long_decode_bf16,decode_fp8",
+                    help="comma list of workloads reported under 'secondary' ('' for none)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path shards by request or kv head with no exchange)"}))
+        sys.exit(2)
+    import torch
+
+    import flashattention_paged_kv_amd as pkv
+    import workloads
+
+    pkv.load_library()  # fails loudly when the HIP library is missing
+    runner, ms, value, roof = measure(args.workload, args.steps, args.warmup, args.layers, torch, pkv, workloads)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": UNITS[args.workload], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3" if getattr(runner, "fp8", False) else "bf16",
+        "data": "synthetic", "config": runner.describe(), "roofline": roof,
+    }
+    secondary = {}
+    for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
+        try:
+            r2, ms2, v2, roof2 = measure(name, max(args.steps // 2, 5), max(args.warmup // 2, 2), 0, torch, pkv,
+                                         workloads)
+            secondary[name] = {"value": round(v2, 2), "unit": UNITS[name], "ms_per_step": round(ms2, 4),
+                               "config": r2.describe(), "roofline": roof2}
+            del r2
+        except Exception as e:  # a workload whose kernel is missing is reported, not hidden
+            secondary[name] = {"error": f"{type(e).__name__}: {e}"}
+        torch.cuda.empty_cache()
+    if secondary:
+        line["secondary"] = secondary
+    if not args.no_cpu_baseline and hasattr(runner, "cpu_baseline"):
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            cores = 1
+        cb = runner.cpu_baseline(args.cpu_budget, oracle)
+        cb.update({"cores": cores, "kind": "oracle"})
+        line["cpu_baseline"] = cb
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+"""ctypes binding of libpkv (argument marshalling only).
+
+Each function takes torch tensors that already live on the GPU, checks their
+dtype / shape / contiguity, and forwards raw device pointers and torch's
+current HIP stream to the C entry point of the same name.  All arithmetic
+runs in the library's kernels; there is no fallback: if ``libpkv.so`` is
+missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
+PKV_BF16, PKV_FP8_E4M3 = 0, 1
+PKV_DECODE, PKV_EXTEND = 0, 1
+
+EXPORTED = ("pkv_workspace_size", "pkv_plan_metadata", "pkv_kv_store", "pkv_attn_decode",
+            "pkv_attn_extend", "pkv_last_error", "pkv_version")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"pkv error {code}: {msg}")
+        self.code = code
+        self.msg = msg
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("q_block", ctypes.c_int32),
+                ("k_block", ctypes.c_int32), ("max_kv_len", ctypes.c_int32),
+                ("kv_chunk", ctypes.c_int32), ("split_target", ctypes.c_int32)]
+
+    def __init__(self, num_q_heads, num_kv_heads, head_dim, page_size, max_kv_len,
+                 kv_dtype=PKV_BF16, q_block=0, k_block=0, kv_chunk=0, split_target=0):
+        super().__init__(num_q_heads, num_kv_heads, head_dim, page_size, kv_dtype, q_block,
+                         k_block, max_kv_len, kv_chunk, split_target)
+
+
+_P = ctypes.c_void_p
+_I32, _I64, _SZ, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpkv.so (built in-tree by ``build.py``); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m flashattention_paged_kv_amd.build` "
+                           "(the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(path)
+    pp = ctypes.POINTER(Params)
+    lib.pkv_workspace_size.argtypes = [pp, _I32, _I32, _I64, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
+    lib.pkv_plan_metadata.argtypes = [pp, _I32, _I32, _I64, _P, _P, _P, _SZ, _P]
+    lib.pkv_kv_store.argtypes = [pp, _P, _P, _I64, _P, _P, _P, _I64, _P]
+    lib.pkv_attn_decode.argtypes = [pp, _P, _P, _P, _P, _P, _I64, _P, _I64, _P, _P, _I32, _F,
+                                    _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]
+    lib.pkv_attn_extend.argtypes = [pp, _P, _P, _P, _P, _P, _I64, _P, _I64, _P, _P, _P, _I32, _I64,
+                                    _F, _P, _SZ, _P, _SZ, _P]
+    for f in ("pkv_workspace_size", "pkv_plan_metadata", "pkv_kv_store", "pkv_attn_decode",
+              "pkv_attn_extend", "pkv_version"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().pkv_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != PKV_OK:
+        raise PkvError(rc, last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None, ndim=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def workspace_size(params: Params, mode: int, max_batch: int, max_total_q: int = 0) -> Tuple[int, int]:
+    lib = load_library()
+    ws, sc = _SZ(0), _SZ(0)
+    _check(lib.pkv_workspace_size(ctypes.byref(params), mode, max_batch, max_total_q, ctypes.byref(ws),
+                                  ctypes.byref(sc)))
+    return ws.value, sc.value
+
+
+@dataclass
+class Plan:
+    """Output of :func:`plan_metadata`: the device workspace and what it was planned for."""
+    workspace: "object"
+    mode: int
+    batch: int
+    total_q: int
+    scratch_bytes: int
+
+
+def plan_metadata(params: Params, mode: int, seq_lens, cu_seqlens_q=None, total_q: int = 0,
+                  workspace=None) -> Plan:
+    import torch
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    batch = seq_lens.shape[0]
+    ws_bytes, sc_bytes = workspace_size(params, mode, batch, total_q if mode == PKV_EXTEND else 0)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=seq_lens.device)
+    _need(workspace, "workspace")
+    lib = load_library()
+    _check(lib.pkv_plan_metadata(ctypes.byref(params), mode, batch, total_q, _ptr(seq_lens), _ptr(cu_seqlens_q),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return Plan(workspace, mode, batch, total_q, sc_bytes)
+
+
+def kv_store(params: Params, k_pool, v_pool, k_new, v_new, slots):
+    import torch
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, ndim=3)
+    _need(slots, "slots", torch.int32, 1)
+    if k_new.shape[0] != slots.shape[0] or v_new.shape[0] != slots.shape[0]:
+        raise ValueError("k_new/v_new rows must match slots")
+    lib = load_library()
+    _check(lib.pkv_kv_store(ctypes.byref(params), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0], _ptr(k_new),
+                            _ptr(v_new), _ptr(slots), slots.shape[0], _stream()))
+
+
+def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan: Plan, scratch=None,
+                out=None, lse=None, sm_scale: Optional[float] = None, req_pool_indices=None,
+                sfq=None, sfk=None, sfv=None, v_mean=None):
+    """Decode attention: q [B, Hq, d] (bf16, or uint8 E4M3 codes) -> out [B, Hq, d] bf16."""
+    import torch
+    _need(q, "q", ndim=3)
+    _need(req_to_token, "req_to_token", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(req_pool_indices, "req_pool_indices", torch.int32, 1)
+    for t, n in ((sfq, "sfq"), (sfk, "sfk"), (sfv, "sfv"), (v_mean, "v_mean"), (lse, "lse")):
+        _need(t, n, torch.float32)
+    B = seq_lens.shape[0]
+    if plan.mode != PKV_DECODE or plan.batch != B:
+        raise ValueError("plan was not made by plan_metadata(PKV_DECODE) for this batch")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    if scratch is None:
+        scratch = torch.empty(max(plan.scratch_bytes, 16), dtype=torch.uint8, device=q.device)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(params.head_dim)
+    lib = load_library()
+    ws = plan.workspace
+    _check(lib.pkv_attn_decode(ctypes.byref(params), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                               k_pool.shape[0], _ptr(req_to_token), req_to_token.shape[1], _ptr(req_pool_indices),
+                               _ptr(seq_lens), B, float(sm_scale), _ptr(sfq), _ptr(sfk), _ptr(sfv), _ptr(v_mean),
+                               _ptr(ws), ws.numel() * ws.element_size(), _ptr(scratch),
+                               scratch.numel() * scratch.element_size(), _stream()))
+    return out
+
+
+def attn_extend(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, cu_seqlens_q, plan: Plan,
+                out=None, lse=None, sm_scale: Optional[float] = None, req_pool_indices=None):
+    """Causal extend attention: q [total_q, Hq, d] bf16 -> out [total_q, Hq, d] bf16."""
+    import torch
+    _need(q, "q", torch.bfloat16, 3)
+    _need(req_to_token, "req_to_token", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _need(req_pool_indices, "req_pool_indices", torch.int32, 1)
+    _need(lse, "lse", torch.float32)
+    B = seq_lens.shape[0]
+    total_q = q.shape[0]
+    if plan.mode != PKV_EXTEND or plan.batch != B or plan.total_q != total_q:
+        raise ValueError("plan was not made by plan_metadata(PKV_EXTEND) for this batch and total_q")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(params.head_dim)
+    lib = load_library()
+    ws = plan.workspace
+    _check(lib.pkv_attn_extend(ctypes.byref(params), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                               k_pool.shape[0], _ptr(req_to_token), req_to_token.shape[1], _ptr(req_pool_indices),
+                               _ptr(seq_lens), _ptr(cu_seqlens_q), B, total_q, float(sm_scale), _ptr(ws),
+                               ws.numel() * ws.element_size(), None, 0, _stream()))
+    return out

@@ -1,0 +1,239 @@
+// Split-KV paged decode, bf16 K/V, fp32 accumulation (one query row per
+// request).  HBM-bound: every K/V byte of a request is read exactly once.
+//
+// One wave64 per work item (request b, one split of its KV range, kv head g,
+// group of up to 16 query heads of g).  The wave walks its range in 32-token
+// tiles; every tile is gathered straight from the pools into registers
+// through req_to_token (a slot lookup per token, so any page size works):
+//
+//  * scores use the MFMA 16x16x32 bf16 product Sᵀ = K·Qᵀ: K rows are the A
+//    operand (one 16-byte load per lane and 32-wide d chunk), the query
+//    heads of the group are the B operand, kept in registers for the item;
+//  * the Sᵀ output leaves every lane with 4+4 scores of ONE head, so the
+//    online softmax (running max m, sum l, rescale of the accumulator) is
+//    per-lane arithmetic plus two xor-shuffles for the tile max, and the
+//    probabilities are already in the B-operand layout of the PV product;
+//  * PV is Oᵀ = Vᵀ·Pᵀ with Vᵀ as the A operand: each lane loads 8 V rows
+//    (16 bytes of each) and transposes them to operands with byte permutes,
+//    so no LDS round trip is needed.
+//
+// Items with one split write bf16 O and lse directly; otherwise the split's
+// normalised partial O and log2-sum-exp go to scratch and the merge kernel
+// combines them (log-sum-exp algebra, fixed order, deterministic).
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+
+template <int D>
+struct KVTile {
+  static constexpr int KB = D / 32;
+  u32x4 k[2][KB];  // A operands of Sᵀ = K·Qᵀ: [token block][32-wide d chunk]
+  u32x4 v[8];      // the lane's 8 V rows, elements d = 8*(lane%16) .. +8
+};
+
+// Lane l's token slot for positions t0 + (l & 31) of the tile (-1 past the range).
+__device__ __forceinline__ int tile_slot(const int32_t* __restrict__ rtt_row, int t0, int kv_end,
+                                         int64_t pool_slots, int lane) {
+  const int tok = t0 + (lane & 31);
+  return tok < kv_end ? clamp_slot(rtt_row[tok], pool_slots) : -1;
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile(KVTile<D>& t, int slot, const uint16_t* __restrict__ kbase,
+                                          const uint16_t* __restrict__ vbase, int64_t row_elems, int lane) {
+  constexpr int KB = D / 32;
+  const int l16 = lane & 15, j = lane >> 4;
+  const int sk0 = __shfl(slot, l16), sk1 = __shfl(slot, 16 + l16);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    t.k[0][kb] = sk0 >= 0 ? ldg16(kbase + (int64_t)sk0 * row_elems + 32 * kb + 8 * j) : z;
+    t.k[1][kb] = sk1 >= 0 ? ldg16(kbase + (int64_t)sk1 * row_elems + 32 * kb + 8 * j) : z;
+  }
+  const bool d_ok = (D == 128) || (l16 < D / 8);
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int tau = r < 4 ? 4 * j + r : 16 + 4 * j + (r - 4);
+    const int sv = __shfl(slot, tau);
+    t.v[r] = (sv >= 0 && d_ok) ? ldg16(vbase + (int64_t)sv * row_elems + 8 * l16) : z;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void compute_tile(const KVTile<D>& t, const u32x4 (&qop)[D / 32], int t0, int kv_end,
+                                             float scale_log2, float& m, float& lpart, floatx4 (&acc)[8],
+                                             int lane) {
+  constexpr int KB = D / 32;
+  const int j = lane >> 4;
+  floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    s0 = mfma16x16x32(as_bf16x8(t.k[0][kb]), as_bf16x8(qop[kb]), s0);
+    s1 = mfma16x16x32(as_bf16x8(t.k[1][kb]), as_bf16x8(qop[kb]), s1);
+  }
+  float sc[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sc[r] = (t0 + 4 * j + r < kv_end) ? s0[r] * scale_log2 : kNegInf;
+    sc[4 + r] = (t0 + 16 + 4 * j + r < kv_end) ? s1[r] * scale_log2 : kNegInf;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m, mx);  // finite: token t0 of the tile is always in range
+  const float alpha = exp2_fast(m - m_new);
+  m = m_new;
+  float p[8];
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = exp2_fast(sc[i] - m_new);
+    ps += p[i];
+  }
+  lpart = lpart * alpha + ps;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+  u32x4 pop;
+  pop[0] = pack_bf16x2(p[0], p[1]);
+  pop[1] = pack_bf16x2(p[2], p[3]);
+  pop[2] = pack_bf16x2(p[4], p[5]);
+  pop[3] = pack_bf16x2(p[6], p[7]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int w = e >> 1;
+    u32x4 vop;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      vop[k] = (e & 1) ? pack_hi16(t.v[2 * k][w], t.v[2 * k + 1][w]) : pack_lo16(t.v[2 * k][w], t.v[2 * k + 1][w]);
+    acc[e] = mfma16x16x32(as_bf16x8(vop), as_bf16x8(pop), acc[e]);
+  }
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(DecodeArgs a) {
+  constexpr int KB = D / 32;
+  const int32_t* __restrict__ ws = a.ws;
+  if ((int)blockIdx.x >= ws[WS_NUM_ITEMS]) return;
+  const int4 it = reinterpret_cast<const int4*>(ws + a.items_off)[blockIdx.x];
+  const int b = it.x, kv_begin = it.y, kv_end = it.z, part = it.w;
+  const int g = blockIdx.y / a.head_groups, hg = blockIdx.y - g * a.head_groups;
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, j = lane >> 4;
+  const int hl = hg * 16 + l16;
+  const bool head_ok = hl < a.group;
+  const int h = g * a.group + hl;
+  const int row = a.rpi ? a.rpi[b] : b;
+  const int32_t* __restrict__ rtt_row = a.rtt + (int64_t)row * a.rtt_stride;
+  const int64_t row_elems = (int64_t)a.hkv * D;
+  const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * D;
+  const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * D;
+
+  u32x4 qop[KB];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (head_ok ? h : 0)) * D;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) qop[kb] = head_ok ? ldg16(qrow + 32 * kb + 8 * j) : z;
+  }
+
+  float m = kNegInf, lpart = 0.f;
+  floatx4 acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (kv_begin < kv_end) {
+    KVTile<D> cur, nxt;
+    int slot_n = tile_slot(rtt_row, kv_begin, kv_end, a.pool_slots, lane);
+    load_tile<D>(cur, slot_n, kbase, vbase, row_elems, lane);
+    slot_n = tile_slot(rtt_row, kv_begin + kDecodeTile, kv_end, a.pool_slots, lane);
+    for (int t0 = kv_begin; t0 < kv_end; t0 += kDecodeTile) {
+      const int slot_nn = tile_slot(rtt_row, t0 + 2 * kDecodeTile, kv_end, a.pool_slots, lane);
+      load_tile<D>(nxt, slot_n, kbase, vbase, row_elems, lane);
+      compute_tile<D>(cur, qop, t0, kv_end, a.scale_log2, m, lpart, acc, lane);
+      cur = nxt;
+      slot_n = slot_nn;
+    }
+  }
+
+  float l = lpart + __shfl_xor(lpart, 16);
+  l += __shfl_xor(l, 32);
+  if (!head_ok) return;
+  const bool rows_ok = (D == 128) || (j < 2);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse2 = l > 0.f ? m + __log2f(l) : kNegInf;
+  if (part < 0) {
+    if (rows_ok) {
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.hq + h) * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(acc[2 * k][r] * inv, acc[2 * k + 1][r] * inv);
+        stg16(orow + 32 * j + 8 * r, w);
+      }
+    }
+    if (j == 0 && a.lse) a.lse[(int64_t)b * a.hq + h] = lse2 * kLn2;
+  } else {
+    if (rows_ok) {
+      float* po = a.part_o + ((int64_t)part * a.hq + h) * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        floatx4 w0 = {acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
+        floatx4 w1 = {acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv};
+        *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r) = w0;
+        *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r + 4) = w1;
+      }
+    }
+    if (j == 0) a.part_lse[(int64_t)part * a.hq + h] = lse2;
+  }
+}
+
+// Combine the split partials of requests with more than one split:
+// lse = log Σ_s exp(lse_s), O = Σ_s exp(lse_s - lse)·O_s (partials in log2 units).
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+  const int b = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int32_t* __restrict__ req = a.ws + a.req_off;
+  const int s0 = req[b];
+  int s1 = req[b + 1];
+  const int num = a.ws[WS_NUM_ITEMS];
+  s1 = s1 < num ? s1 : num;
+  if (s1 - s0 <= 1) return;
+  float M = kNegInf;
+  for (int s = s0; s < s1; ++s) M = fmaxf(M, a.part_lse[(int64_t)s * a.hq + h]);
+  float tot = 0.f, o = 0.f;
+  for (int s = s0; s < s1; ++s) {
+    const float ls = a.part_lse[(int64_t)s * a.hq + h];
+    const float w = ls == kNegInf ? 0.f : exp2_fast(ls - M);
+    tot += w;
+    o += w * a.part_o[((int64_t)s * a.hq + h) * D + d];
+  }
+  const float res = tot > 0.f ? o / tot : 0.f;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.hq + h) * D;
+  orow[d] = (uint16_t)(pack_bf16x2(res, 0.f) & 0xffffu);
+  if (d == 0 && a.lse) a.lse[(int64_t)b * a.hq + h] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : kNegInf;
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
+                              hipStream_t s) {
+  if (capacity <= 0 || batch <= 0) return hipSuccess;
+  dim3 grid((unsigned)capacity, (unsigned)(a.hkv * a.head_groups));
+  if (head_dim == 128) hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int32_t batch, hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
+  dim3 grid((unsigned)batch, (unsigned)a.hq);
+  if (head_dim == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(128), 0, s, a);
+  else hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,179 @@
+// Internal declarations shared by the libpkv translation units: workspace
+// layout, kernel argument blocks and device helpers for gfx950.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------- constants
+constexpr int kDecodeTile = 32;       // decode tokens per inner step (two 16-token MFMA blocks)
+constexpr int kDefaultSplitTarget = 4096;
+constexpr int kExtendRows = 128;      // (head, token) rows per extend work item (4 waves x 32)
+constexpr int kExtendTileN = 64;      // keys per extend inner step
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanLdsSortMax = 4096; // extend items sorted in LDS (32 KiB) up to this count
+
+// Workspace header words (int32).
+enum : int {
+  WS_MODE = 0,
+  WS_BATCH = 1,
+  WS_NUM_ITEMS = 2,
+  WS_CAPACITY = 3,
+  WS_CHUNK = 4,  // decode: chunk tiles; extend: block tokens
+  WS_HEADER_INTS = 16
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t align_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// Layout of the plan workspace, in int32 words from its start.
+struct WsLayout {
+  int64_t req_off = WS_HEADER_INTS;  // [B+1] split / tile offsets
+  int64_t items_off = 0;             // [cap][4] work items
+  int64_t tmp_off = 0;               // extend: unsorted items [cap][4]
+  int64_t keys_off = 0;              // extend: u64 sort keys [pow2(cap)] (8-byte aligned)
+  int64_t total_ints = 0;
+  int64_t capacity = 0;
+};
+
+inline int64_t next_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+inline int64_t decode_capacity(const pkv_params& p, int64_t batch) {
+  const int64_t group = p.num_q_heads / p.num_kv_heads;
+  const int64_t units = (int64_t)p.num_kv_heads * ceil_div(group, 16);
+  const int64_t tgt = p.split_target > 0 ? p.split_target : kDefaultSplitTarget;
+  const int64_t max_tiles = ceil_div(p.max_kv_len, kDecodeTile) > 0 ? ceil_div(p.max_kv_len, kDecodeTile) : 1;
+  if (p.kv_chunk > 0) {
+    int64_t per = ceil_div(p.max_kv_len, p.kv_chunk);
+    return batch * (per > 0 ? per : 1);
+  }
+  int64_t target_splits = ceil_div(tgt, units);
+  if (target_splits < 1) target_splits = 1;
+  int64_t a = target_splits + batch, b = batch * max_tiles;
+  return a < b ? a : b;
+}
+
+inline int extend_block_tokens(const pkv_params& p) {
+  int group = p.num_q_heads / p.num_kv_heads;
+  int bt = kExtendRows / group;
+  return bt > 0 ? bt : 1;
+}
+
+inline int64_t extend_capacity(const pkv_params& p, int64_t batch, int64_t total_q) {
+  return ceil_div(total_q, extend_block_tokens(p)) + batch;
+}
+
+inline WsLayout ws_layout(const pkv_params& p, int mode, int64_t batch, int64_t total_q) {
+  WsLayout w;
+  w.req_off = WS_HEADER_INTS;
+  w.items_off = align_up(w.req_off + batch + 1, 4);
+  if (mode == PKV_DECODE) {
+    w.capacity = decode_capacity(p, batch);
+    w.total_ints = w.items_off + 4 * w.capacity;
+  } else {
+    w.capacity = extend_capacity(p, batch, total_q);
+    w.tmp_off = w.items_off + 4 * w.capacity;
+    w.keys_off = align_up(w.tmp_off + 4 * w.capacity, 2);
+    w.total_ints = w.keys_off + 2 * next_pow2(w.capacity > 0 ? w.capacity : 1);
+  }
+  return w;
+}
+
+// Decode scratch: split partials, fp32.
+struct DecodeScratch {
+  int64_t part_o_bytes = 0;
+  int64_t part_lse_off = 0;
+  int64_t total_bytes = 0;
+};
+
+inline DecodeScratch decode_scratch(const pkv_params& p, int64_t batch) {
+  DecodeScratch s;
+  const int64_t cap = decode_capacity(p, batch);
+  s.part_o_bytes = align_up(cap * p.num_q_heads * p.head_dim * (int64_t)sizeof(float), 256);
+  s.part_lse_off = s.part_o_bytes;
+  s.total_bytes = s.part_o_bytes + align_up(cap * p.num_q_heads * (int64_t)sizeof(float), 256);
+  return s;
+}
+
+// ---------------------------------------------------------------- kernel args
+struct PlanArgs {
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;
+  int32_t* ws;
+  int64_t req_off, items_off, tmp_off, keys_off;
+  int64_t capacity;
+  int64_t total_q;
+  int32_t batch;
+  int32_t mode;
+  int32_t max_kv_len;
+  int32_t kv_chunk;
+  int32_t target_splits;
+  int32_t block_tokens;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* rtt;
+  const int32_t* rpi;
+  const int32_t* ws;
+  void* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  const float* sfq;
+  const float* sfk;
+  const float* sfv;
+  const float* v_mean;
+  int64_t rtt_stride;
+  int64_t pool_slots;
+  int64_t items_off;
+  int64_t req_off;
+  int32_t hq, hkv, group, head_groups;
+  int32_t k_block, sfk_stride;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+struct ExtendArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* rtt;
+  const int32_t* rpi;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;
+  const int32_t* ws;
+  void* out;
+  float* lse;
+  int64_t rtt_stride;
+  int64_t pool_slots;
+  int64_t items_off;
+  int64_t total_q;
+  int32_t hq, hkv, group, block_tokens;
+  int32_t max_kv_len;
+  float scale_log2;
+};
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_kv_store(void* k_pool, void* v_pool, int64_t pool_slots, const void* k_new,
+                           const void* v_new, const int32_t* slots, int64_t num_tokens,
+                           int64_t row_bytes, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
+                              hipStream_t s);
+hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
+                             hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int32_t batch, hipStream_t s);
+hipError_t launch_extend_bf16(const ExtendArgs& a, int head_dim, int64_t capacity, hipStream_t s);
+
+}  // namespace pkv

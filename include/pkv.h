@@ -1,0 +1,169 @@
+/*
+ * pkv.h — C ABI of libpkv: paged-KV FlashAttention (EXTEND and DECODE) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes softmax(S)·V with S = sm_scale·Q·Kᵀ, reading K and V
+ * through a two-level paged KV cache, and never writes S to device memory:
+ *
+ *   - the attention definition and the reason for tiling it (the score
+ *     matrix must not live in HBM) follow the FlashAttention part of the
+ *     page "FlashAttention: 优化计算过程中的临时显存占用" (§1 and §2);
+ *   - the two-level cache follows "Implement Flash Attention Back End in
+ *     SGLang – Basics and KV Cache" (KV-cache part) and "Flash Attention
+ *     Backend in SGLang: Grundlagen und KV Cache optimal nutzen" (KV-cache
+ *     paragraph): req_to_token maps (request row, position) to a KV slot,
+ *     and each layer's K pool and V pool map a slot to a row [Hkv, d];
+ *   - EXTEND (new tokens appended to a cached prefix, causal) and DECODE
+ *     (one new token per request) are the two forward modes of the same
+ *     pages;
+ *   - the scheduling metadata is computed once per batch and reused by every
+ *     layer, as in "SGLang의 FA3 디코드 최적화: get_scheduler_metadata 도입"
+ *     (intro and code §1-§3);
+ *   - the optional 8-bit decode follows the Sage formula of "FlashInfer
+ *     PrimTS, Sage Attention 도입으로 8비트 양자화 및 성능 최적화 달성"
+ *     (code §1, §4, §5).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   B          batch (requests in the call), Hq / Hkv query / KV heads,
+ *              G = Hq / Hkv (query head h reads KV head h / G), d = head_dim.
+ *   seq_lens   int32 [B] device: L_b, the KV length attended by request b,
+ *              INCLUDING this step's new tokens (store them with
+ *              pkv_kv_store first).
+ *   cu_seqlens_q int32 [B+1] device (EXTEND): new-token rows of request b
+ *              are q rows [cu[b], cu[b+1]); n_b = cu[b+1]-cu[b], the cached
+ *              prefix is p_b = L_b - n_b and new token i sees keys 0..p_b+i.
+ *   req_to_token int32 [rows, rtt_stride] device: slot of position j of
+ *              request b is req_to_token[row(b) * rtt_stride + j], with
+ *              row(b) = req_pool_indices[b] (or b when that pointer is NULL).
+ *   pools      K and V pools of ONE layer, [pool_slots, Hkv, d] row-major,
+ *              bf16 (or E4M3 bytes for the 8-bit decode).
+ *   q / out    [T, Hq, d] row-major (T = B in DECODE); out is bf16; lse is
+ *              float [T, Hq], natural-log log-sum-exp of the scaled scores
+ *              (-inf for a row with no keys), optional (NULL).
+ *   stream     a hipStream_t passed as void* (NULL = default stream).
+ *
+ * Ownership and execution: the caller allocates and frees every buffer; the
+ * library allocates no device memory and keeps no mutable global state other
+ * than the thread-local error text.  Every call validates its host
+ * arguments, then enqueues kernels on `stream` and returns without
+ * synchronising.  Grids depend only on host arguments, never on device
+ * values, so calls can be captured in a HIP graph.
+ *
+ * Errors: a non-zero pkv_status means nothing was enqueued (PKV_EHIP: a
+ * launch failed); pkv_last_error() describes the last failure of the calling
+ * thread.  Device-side VALUES are not validated (as the Sage page states for
+ * its scales): seq_lens are clamped to [0, max_kv_len], query row ranges to
+ * [0, total_q], and slots outside [0, pool_slots) are clamped when read and
+ * skipped when written, so bad values give wrong numbers but never an
+ * out-of-bounds access.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* malformed argument (NULL, negative size, ...) */
+  PKV_EUNSUPPORTED = 2,  /* well formed but not implemented (head_dim, dtype, ...) */
+  PKV_EWORKSPACE = 3,    /* workspace or scratch smaller than required */
+  PKV_EHIP = 4           /* a HIP launch failed */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_BF16 = 0,
+  PKV_FP8_E4M3 = 1 /* OCP E4M3FN: 1-4-3, bias 7, largest finite 448 */
+} pkv_dtype;
+
+typedef enum pkv_mode { PKV_DECODE = 0, PKV_EXTEND = 1 } pkv_mode;
+
+/* Plan-time description of the attention problem (cf. the Sage page, code
+ * §5: block sizes are fixed when planning, scales are supplied per run). */
+typedef struct pkv_params {
+  int32_t num_q_heads;  /* Hq >= 1 */
+  int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;     /* d: 64 or 128 */
+  int32_t page_size;    /* power of two in [1, 256]; informational (reads are per token) */
+  int32_t kv_dtype;     /* pkv_dtype; PKV_FP8_E4M3 only for DECODE */
+  int32_t q_block;      /* 8-bit: q rows per sfQ block (DECODE uses one row per request); else 0 */
+  int32_t k_block;      /* 8-bit: key positions per sfK block, a multiple of 16; else 0 */
+  int32_t max_kv_len;   /* upper bound of seq_lens (>= 1, <= rtt_stride of the run calls) */
+  int32_t kv_chunk;     /* DECODE split size in tokens: 0 = automatic, else a multiple of 32 */
+  int32_t split_target; /* DECODE automatic mode: target work items per call (0 = 4096) */
+} pkv_params;
+
+/* Sizes of the plan workspace (written by pkv_plan_metadata, read by the run
+ * calls of every layer) and of the per-call scratch (split partials) for a
+ * batch of at most `max_batch` requests and `max_total_q` new-token rows.
+ * Neither grows with the square of the sequence length.  Host pointers out. */
+int pkv_workspace_size(const pkv_params* params, int32_t mode, int32_t max_batch,
+                       int64_t max_total_q, size_t* workspace_bytes, size_t* scratch_bytes);
+
+/* Once per batch (SGLang get_scheduler_metadata page, code §1-§3 and the
+ * "why" part): from seq_lens (and cu_seqlens_q for EXTEND) compute the
+ * split-KV / query-tile work list into `workspace` (device, >=
+ * workspace_bytes).  One kernel launch; the result is reused unchanged by
+ * every layer's pkv_attn_* call with the same batch.  DECODE ignores
+ * cu_seqlens_q (may be NULL) and total_q. */
+int pkv_plan_metadata(const pkv_params* params, int32_t mode, int32_t batch, int64_t total_q,
+                      const int32_t* seq_lens, const int32_t* cu_seqlens_q, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Store this step's new K/V rows (KV-cache paragraph of the SGLang pages:
+ * the cache is updated inside the forward pass):
+ * k_pool[slots[t]] = k_new[t] and v_pool[slots[t]] = v_new[t] for
+ * t < num_tokens, each row [Hkv, d] of the params' kv_dtype.  k_new/v_new
+ * are [num_tokens, Hkv, d] device buffers; slots int32 [num_tokens] device,
+ * distinct.  A slot outside [0, pool_slots) is skipped. */
+int pkv_kv_store(const pkv_params* params, void* k_pool, void* v_pool, int64_t pool_slots,
+                 const void* k_new, const void* v_new, const int32_t* slots, int64_t num_tokens,
+                 void* stream);
+
+/* DECODE: one query row per request (q, out: [B, Hq, d]).  bf16 path: q and
+ * pools bf16, sfq/sfk/sfv/v_mean must be NULL.  8-bit path (kv_dtype ==
+ * PKV_FP8_E4M3): q and pools hold E4M3 bytes and the Sage formula applies:
+ * S = sm_scale·sfq[b,h]·sfk[b,g,j/k_block]·(q8·k8), P stored as E4M3 of
+ * 448·exp(S - m), O = sfv[b,g,:]·(Σ P8·v8)/(448·l) (+ v_mean[b,g,:]), where l
+ * sums the unquantised exp(S - m).  sfq float [B, Hq], sfk float
+ * [B, Hkv, sfk_stride] with sfk_stride = ceil(max_kv_len / k_block), sfv and
+ * v_mean float [B, Hkv, d]; v_mean may be NULL.  Scale values are not checked.
+ * `workspace` comes from pkv_plan_metadata(PKV_DECODE) for this batch;
+ * `scratch` (device, >= scratch_bytes) holds split partials and may be
+ * reused by the next call on the same stream. */
+int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void* q,
+                    const void* k_pool, const void* v_pool, int64_t pool_slots,
+                    const int32_t* req_to_token, int64_t rtt_stride, const int32_t* req_pool_indices,
+                    const int32_t* seq_lens, int32_t batch, float sm_scale, const float* sfq,
+                    const float* sfk, const float* sfv, const float* v_mean,
+                    const void* workspace, size_t workspace_bytes, void* scratch,
+                    size_t scratch_bytes, void* stream);
+
+/* EXTEND: causal attention of the total_q new-token rows (q, out:
+ * [total_q, Hq, d] bf16) over their request's cached prefix and themselves,
+ * bf16 pools.  `workspace` comes from pkv_plan_metadata(PKV_EXTEND) with the
+ * same batch and total_q.  `scratch` is not used (may be NULL). */
+int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void* q,
+                    const void* k_pool, const void* v_pool, int64_t pool_slots,
+                    const int32_t* req_to_token, int64_t rtt_stride, const int32_t* req_pool_indices,
+                    const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t batch,
+                    int64_t total_q, float sm_scale, const void* workspace, size_t workspace_bytes,
+                    void* scratch, size_t scratch_bytes, void* stream);
+
+/* Text of the calling thread's last error ("" if none).  Valid until the
+ * thread's next pkv_* call. */
+const char* pkv_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pkv_version(void);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* PKV_H_ */

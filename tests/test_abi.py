@@ -1,0 +1,142 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/pkv.h declares, and rejects bad host arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flashattention_paged_kv_amd as pkv
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pkv.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(pkv.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _ws(lib, params, mode=pkv.PKV_DECODE, batch=4, total_q=0):
+    ws, sc = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    rc = lib.pkv_workspace_size(ctypes.byref(params), mode, batch, total_q, ctypes.byref(ws), ctypes.byref(sc))
+    return rc, ws.value, sc.value
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(num_q_heads=30, num_kv_heads=8), pkv.PKV_EINVAL, "is not a multiple of"),
+    (dict(num_q_heads=0), pkv.PKV_EINVAL, "must be >= 1"),
+    (dict(head_dim=96), pkv.PKV_EUNSUPPORTED, "head_dim=96 is unsupported"),
+    (dict(page_size=24), pkv.PKV_EINVAL, "power of two"),
+    (dict(page_size=512), pkv.PKV_EINVAL, "power of two"),
+    (dict(max_kv_len=0), pkv.PKV_EINVAL, "max_kv_len"),
+    (dict(kv_chunk=48), pkv.PKV_EINVAL, "kv_chunk"),
+    (dict(k_block=16), pkv.PKV_EINVAL, "k_block is unsupported by a bf16 plan"),
+    (dict(q_block=1), pkv.PKV_EINVAL, "q_block is unsupported by a bf16 plan"),
+    (dict(kv_dtype=7), pkv.PKV_EUNSUPPORTED, "kv_dtype=7"),
+    (dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=20, q_block=1), pkv.PKV_EINVAL, "k_block=20"),
+    (dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=64, q_block=1, head_dim=64), pkv.PKV_EUNSUPPORTED, "head_dim=128"),
+])
+def test_params_validation(lib, kw, code, msg):
+    base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_kv_len=4096)
+    base.update(kw)
+    p = pkv.Params(**base)
+    rc, _, _ = _ws(lib, p)
+    assert rc == code
+    assert msg in pkv.last_error()
+
+
+def test_fp8_extend_is_rejected_at_plan_time(lib):
+    p = pkv.Params(32, 8, 128, 16, 4096, kv_dtype=pkv.PKV_FP8_E4M3, q_block=1, k_block=64)
+    rc, _, _ = _ws(lib, p, mode=pkv.PKV_EXTEND, total_q=100)
+    assert rc == pkv.PKV_EUNSUPPORTED and "unsupported by an extend plan" in pkv.last_error()
+    rc, ws, sc = _ws(lib, p, mode=pkv.PKV_DECODE)
+    assert rc == pkv.PKV_OK and ws > 0 and sc > 0
+
+
+def test_run_call_argument_errors(lib):
+    p = pkv.Params(32, 8, 128, 16, 4096)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    # scales given to a bf16 decode
+    rc = lib.pkv_attn_decode(ctypes.byref(p), fake, None, fake, fake, fake, 100, fake, 4096, None, fake, 4,
+                             0.1, fake, None, None, None, fake, 1 << 20, fake, 1 << 20, None)
+    assert rc == pkv.PKV_EINVAL and "sfq is unsupported by a bf16 plan" in pkv.last_error()
+    # rtt_stride below max_kv_len
+    rc = lib.pkv_attn_decode(ctypes.byref(p), fake, None, fake, fake, fake, 100, fake, 100, None, fake, 4,
+                             0.1, None, None, None, None, fake, 1 << 20, fake, 1 << 20, None)
+    assert rc == pkv.PKV_EINVAL and "rtt_stride" in pkv.last_error()
+    # workspace too small
+    rc = lib.pkv_attn_decode(ctypes.byref(p), fake, None, fake, fake, fake, 100, fake, 4096, None, fake, 4,
+                             0.1, None, None, None, None, fake, 8, fake, 1 << 30, None)
+    assert rc == pkv.PKV_EWORKSPACE and "workspace_bytes=8" in pkv.last_error()
+    # non-finite scale
+    rc = lib.pkv_attn_decode(ctypes.byref(p), fake, None, fake, fake, fake, 100, fake, 4096, None, fake, 4,
+                             float("nan"), None, None, None, None, fake, 1 << 20, fake, 1 << 20, None)
+    assert rc == pkv.PKV_EINVAL and "sm_scale" in pkv.last_error()
+    # fp8 without scales
+    p8 = pkv.Params(32, 8, 128, 16, 4096, kv_dtype=pkv.PKV_FP8_E4M3, q_block=1, k_block=64)
+    rc = lib.pkv_attn_decode(ctypes.byref(p8), fake, None, fake, fake, fake, 100, fake, 4096, None, fake, 4,
+                             0.1, None, None, None, None, fake, 1 << 20, fake, 1 << 20, None)
+    assert rc == pkv.PKV_EINVAL and "needs sfq, sfk and sfv" in pkv.last_error()
+    # misaligned pointer
+    odd = ctypes.c_void_p(0x1002)
+    rc = lib.pkv_attn_decode(ctypes.byref(p), fake, None, odd, fake, fake, 100, fake, 4096, None, fake, 4,
+                             0.1, None, None, None, None, fake, 1 << 20, fake, 1 << 20, None)
+    assert rc == pkv.PKV_EINVAL and "16-byte aligned" in pkv.last_error()
+    # extend: NULL cu_seqlens_q
+    rc = lib.pkv_attn_extend(ctypes.byref(p), fake, None, fake, fake, fake, 100, fake, 4096, None, fake, None, 4,
+                             64, 0.1, fake, 1 << 20, None, 0, None)
+    assert rc == pkv.PKV_EINVAL and "cu_seqlens_q" in pkv.last_error()
+    # plan: NULL seq_lens, workspace too small
+    rc = lib.pkv_plan_metadata(ctypes.byref(p), pkv.PKV_DECODE, 4, 0, None, None, fake, 1 << 20, None)
+    assert rc == pkv.PKV_EINVAL and "seq_lens" in pkv.last_error()
+    rc = lib.pkv_plan_metadata(ctypes.byref(p), pkv.PKV_DECODE, 4, 0, fake, None, fake, 4, None)
+    assert rc == pkv.PKV_EWORKSPACE
+    # kv_store: negative sizes
+    rc = lib.pkv_kv_store(ctypes.byref(p), fake, fake, 0, fake, fake, fake, 3, None)
+    assert rc == pkv.PKV_EINVAL and "pool_slots" in pkv.last_error()
+    # empty batches are no-ops that succeed without touching the device
+    rc = lib.pkv_attn_decode(ctypes.byref(p), None, None, None, None, None, 100, None, 4096, None, None, 0,
+                             0.1, None, None, None, None, None, 0, None, 0, None)
+    assert rc == pkv.PKV_OK and pkv.last_error() == ""
+
+
+def test_workspace_does_not_grow_with_square_of_length(lib):
+    """O(N) not O(N^2): the plan workspace and decode scratch at 131072 tokens stay
+    far below the materialised score matrix of the FlashAttention memory example."""
+    p = pkv.Params(64, 8, 128, 64, 131072)
+    rc, ws, sc = _ws(lib, p, batch=8)
+    assert rc == 0
+    scores = oracle.score_matrix_bytes(131072, 2, heads=64, batch=8)
+    assert ws + sc < scores / 1000
+    p2 = pkv.Params(64, 8, 128, 64, 2 * 131072)
+    _, ws2, sc2 = _ws(lib, p2, batch=8)
+    assert ws2 + sc2 <= 2 * (ws + sc)
+
+
+def test_capacity_matches_oracle_formula(lib):
+    from oracle.plan import decode_capacity, extend_capacity
+    for (hq, hkv, maxl, chunk, tgt, B) in [(32, 8, 4097, 0, 0, 64), (64, 8, 131073, 0, 0, 8),
+                                           (32, 8, 5000, 64, 0, 37), (40, 2, 700, 0, 64, 5)]:
+        p = pkv.Params(hq, hkv, 128, 16, maxl, kv_chunk=chunk, split_target=tgt)
+        rc, ws, sc = _ws(lib, p, batch=B)
+        cap = decode_capacity(B, hkv, hq // hkv, maxl, chunk, tgt)
+        assert sc >= cap * hq * 129 * 4
+        assert ws >= (16 + B + 1 + 4 * cap) * 4
+    p = pkv.Params(32, 8, 128, 16, 4096)
+    rc, ws, _ = _ws(lib, p, mode=pkv.PKV_EXTEND, batch=16, total_q=17000)
+    assert ws >= 4 * (16 + 17 + 8 * extend_capacity(16, 17000, 4))

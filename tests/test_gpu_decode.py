@@ -1,0 +1,247 @@
+"""GPU parity of the bf16 split-KV decode (plan + kv_store + attn_decode) against
+the fp64 oracle, through the C ABI via the ctypes binding."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (assert_bf16_close, assert_lse_close, dev_bf16, dev_i32, host, torch_mod)
+from workloads import SPECS, Spec, make_device_batch, make_host_batch, permute_pages, pool_before_store, round_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _pkv():
+    import flashattention_paged_kv_amd as pkv
+    return pkv
+
+
+def run_decode(hb, kv_chunk=0, split_target=0, sm_scale=None, req_pool_indices=None, max_kv_len=None,
+               seq_lens_override=None, lse=True):
+    """Upload a host batch (new rows poisoned), plan, store, decode; return host (o, lse, plan)."""
+    torch = torch_mod()
+    pkv = _pkv()
+    lay = hb.layout
+    spec = lay.spec
+    q = round_bf16(hb.q)
+    kp = pool_before_store(round_bf16(hb.k_pool), lay.new_slots)
+    vp = pool_before_store(round_bf16(hb.v_pool), lay.new_slots)
+    k_pool, v_pool = dev_bf16(kp), dev_bf16(vp)
+    k_new, v_new = dev_bf16(round_bf16(hb.k_new)), dev_bf16(round_bf16(hb.v_new))
+    seq = lay.seq_lens if seq_lens_override is None else seq_lens_override
+    params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                        max_kv_len=max_kv_len or max(lay.req_to_token.shape[1], 1),
+                        kv_chunk=kv_chunk, split_target=split_target)
+    seq_d = dev_i32(seq)
+    rtt = dev_i32(lay.req_to_token)
+    plan = pkv.plan_metadata(params, pkv.PKV_DECODE, seq_d)
+    pkv.kv_store(params, k_pool, v_pool, k_new, v_new, dev_i32(lay.new_slots))
+    lse_t = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda") if lse else None
+    rpi = None if req_pool_indices is None else dev_i32(req_pool_indices)
+    out = pkv.attn_decode(params, dev_bf16(q), k_pool, v_pool, rtt, seq_d, plan, sm_scale=sm_scale,
+                          lse=lse_t, req_pool_indices=rpi)
+    torch.cuda.synchronize()
+    return host(out), (lse_t.cpu().numpy().astype(np.float64) if lse else None), plan, (k_pool, v_pool)
+
+
+def oracle_decode(hb, sm_scale=None, seq=None):
+    lay = hb.layout
+    seq = lay.seq_lens if seq is None else seq
+    return oracle.paged_attention(round_bf16(hb.q), round_bf16(hb.k_pool), round_bf16(hb.v_pool),
+                                  lay.req_to_token, seq, np.arange(len(seq) + 1), sm_scale=sm_scale)
+
+
+MEDIUM = Spec("dec_med", "decode", 8, 32, 8, 128, 16, (0, 1500), 1)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_decode_config(seed):
+    hb = make_host_batch(SPECS["tiny_decode"], seed)
+    o, lse, _, _ = run_decode(hb)
+    ro, rlse = oracle_decode(hb)
+    assert_bf16_close(o, ro, "tiny decode")
+    assert_lse_close(lse, rlse, "tiny decode")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("kv_chunk", [0, 32, 256])
+def test_medium_decode_ragged(seed, kv_chunk):
+    hb = make_host_batch(MEDIUM, seed)
+    o, lse, _, _ = run_decode(hb, kv_chunk=kv_chunk)
+    ro, rlse = oracle_decode(hb)
+    assert_bf16_close(o, ro, f"medium decode chunk={kv_chunk}")
+    assert_lse_close(lse, rlse, "medium decode")
+
+
+@pytest.mark.parametrize("hq,hkv,d,page", [(8, 8, 128, 1), (64, 8, 128, 64), (40, 2, 128, 16),
+                                           (16, 4, 64, 16), (12, 4, 64, 2), (32, 8, 64, 256)])
+def test_head_layouts_and_pages(hq, hkv, d, page):
+    spec = Spec("dec_shape", "decode", 5, hq, hkv, d, page, (0, 700), 1)
+    hb = make_host_batch(spec, 3)
+    o, lse, _, _ = run_decode(hb, split_target=64)
+    ro, rlse = oracle_decode(hb)
+    assert_bf16_close(o, ro, f"decode hq={hq} hkv={hkv} d={d} P={page}")
+    assert_lse_close(lse, rlse)
+
+
+def test_custom_scale_and_request_row_indirection():
+    hb = make_host_batch(MEDIUM, 4)
+    lay = hb.layout
+    B = MEDIUM.batch
+    perm = np.random.default_rng(0).permutation(B)
+    # rows of req_to_token are stored permuted; req_pool_indices maps request b -> its row
+    rtt_perm = np.empty_like(lay.req_to_token)
+    rtt_perm[perm] = lay.req_to_token
+    lay.req_to_token = rtt_perm
+    o, lse, _, _ = run_decode(hb, sm_scale=0.05, req_pool_indices=perm)
+    lay.req_to_token = rtt_perm[perm]
+    ro, rlse = oracle_decode(hb, sm_scale=0.05)
+    assert_bf16_close(o, ro, "scale + indirection")
+    assert_lse_close(lse, rlse)
+
+
+def test_forced_split_equals_unsplit_and_runs_are_deterministic():
+    hb = make_host_batch(MEDIUM, 5)
+    o1, l1, _, _ = run_decode(hb, kv_chunk=32)
+    o2, l2, _, _ = run_decode(hb, kv_chunk=32)
+    o3, l3, _, _ = run_decode(hb, kv_chunk=4096)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert np.abs(o1 - o3).max() <= 2e-2
+    assert np.abs(l1 - l3).max() <= 1e-4
+
+
+def test_page_relabelling_is_bit_invariant_on_gpu():
+    hb = make_host_batch(MEDIUM, 6)
+    o1, l1, _, _ = run_decode(hb)
+    lay2, slot_map = permute_pages(hb.layout, np.random.default_rng(1))
+    k2 = np.full_like(hb.k_pool, np.nan)
+    v2 = np.full_like(hb.v_pool, np.nan)
+    k2[slot_map] = hb.k_pool
+    v2[slot_map] = hb.v_pool
+    hb.layout, hb.k_pool, hb.v_pool = lay2, k2, v2
+    o2, l2, _, _ = run_decode(hb)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_one_hot_key_returns_the_value_row_bit_exactly():
+    """Indexing probe: one key aligned with q, the rest zero, so every other weight
+    underflows in fp32 and O must equal that V row exactly."""
+    spec = Spec("onehot", "decode", 4, 8, 2, 128, 16, (40, 300), 1)
+    hb = make_host_batch(spec, 7)
+    lay = hb.layout
+    G = 4
+    rng = np.random.default_rng(3)
+    targets = []
+    for b in range(spec.batch):
+        L = int(lay.seq_lens[b])
+        slots = lay.req_to_token[b, :L]
+        hb.k_pool[slots] = 0.0
+        t = int(rng.integers(0, L))
+        targets.append(slots[t])
+        for g in range(2):
+            qh = hb.q[b, g * G]
+            hb.q[b, g * G:(g + 1) * G] = qh  # all heads of the group share q
+            hb.k_pool[slots[t], g] = qh * (400.0 / float(np.dot(qh, qh)))  # score 400*sm_scale
+    hb.q = round_bf16(hb.q)
+    hb.k_pool = round_bf16(hb.k_pool)
+    hb.v_pool = round_bf16(hb.v_pool)
+    hb.k_new = hb.k_pool[lay.new_slots].copy()
+    o, _, _, _ = run_decode(hb, sm_scale=1.0, kv_chunk=64)
+    for b in range(spec.batch):
+        for h in range(spec.num_q_heads):
+            want = round_bf16(hb.v_pool[targets[b], h // G])
+            assert np.array_equal(o[b, h], want), (b, h)
+
+
+def test_zero_length_request_gives_zero_and_minus_inf():
+    hb = make_host_batch(MEDIUM, 8)
+    seq = hb.layout.seq_lens.copy()
+    seq[3] = 0
+    o, lse, _, _ = run_decode(hb, seq_lens_override=seq, kv_chunk=64)
+    assert np.all(o[3] == 0) and np.all(np.isneginf(lse[3]))
+    ro, rlse = oracle_decode(hb, seq=seq)
+    assert_bf16_close(o, ro, "zero-length row")
+
+
+def test_plan_matches_oracle_rederivation_bit_for_bit():
+    torch = torch_mod()
+    pkv = _pkv()
+    rng = np.random.default_rng(11)
+    for kv_chunk, target in ((0, 0), (0, 100), (64, 0), (0, 50000)):
+        B = 37
+        max_kv = 5000
+        L = rng.integers(0, max_kv + 1, size=B).astype(np.int32)
+        L[5] = max_kv + 100  # clamped
+        params = pkv.Params(32, 8, 128, 16, max_kv_len=max_kv, kv_chunk=kv_chunk, split_target=target)
+        plan = pkv.plan_metadata(params, pkv.PKV_DECODE, dev_i32(L))
+        torch.cuda.synchronize()
+        ws = plan.workspace.cpu().numpy().view(np.int32)
+        ref = oracle.plan_decode(L, 8, 4, max_kv, kv_chunk=kv_chunk, split_target=target)
+        n = ws[2]
+        items_off = -(-(16 + B + 1) // 4) * 4
+        items = ws[items_off:items_off + 4 * n].reshape(-1, 4)
+        assert n == len(ref["items"]) and ws[3] == ref["capacity"] and ws[4] == ref["chunk_tiles"]
+        assert np.array_equal(items, ref["items"])
+        assert np.array_equal(ws[16:16 + B + 1], ref["split_off"])
+
+
+def test_kv_store_round_trip_bit_exact():
+    torch = torch_mod()
+    pkv = _pkv()
+    spec = Spec("st", "extend", 6, 8, 4, 128, 16, (0, 100), (1, 40))
+    hb = make_host_batch(spec, 9)
+    lay = hb.layout
+    params = pkv.Params(8, 4, 128, 16, max_kv_len=lay.max_kv_len)
+    kp = dev_bf16(pool_before_store(hb.k_pool, lay.new_slots, fill=7.0))
+    vp = dev_bf16(pool_before_store(hb.v_pool, lay.new_slots, fill=7.0))
+    before_k = kp.clone()
+    pkv.kv_store(params, kp, vp, dev_bf16(hb.k_new), dev_bf16(hb.v_new), dev_i32(lay.new_slots))
+    torch.cuda.synchronize()
+    k = host(kp)
+    v = host(vp)
+    assert np.array_equal(k[lay.new_slots], hb.k_new) and np.array_equal(v[lay.new_slots], hb.v_new)
+    untouched = np.setdiff1d(np.arange(lay.pool_slots), lay.new_slots)
+    idx = dev_i32(untouched).long()
+    # compare bit patterns: the untouched rows include NaN poison
+    assert torch.equal(kp[idx].view(torch.int16), before_k[idx].view(torch.int16))
+
+
+def _sampled_full_size(name, samples, kv_chunk=0):
+    """Full-size workload on the device, in the bench's launch configuration;
+    a sample of (request, head) outputs is recomputed by the oracle one by one."""
+    torch = torch_mod()
+    pkv = _pkv()
+    spec = SPECS[name]
+    db = make_device_batch(spec, seed=0, layers=1)
+    lay = db.layout
+    params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                        max_kv_len=lay.req_to_token.shape[1], kv_chunk=kv_chunk)
+    plan = pkv.plan_metadata(params, pkv.PKV_DECODE, db.seq_lens)
+    pkv.kv_store(params, db.k_pools[0], db.v_pools[0], db.k_new[0], db.v_new[0], db.new_slots)
+    lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+    out = pkv.attn_decode(params, db.q, db.k_pools[0], db.v_pools[0], db.req_to_token, db.seq_lens, plan, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(0)
+    G = spec.num_q_heads // spec.num_kv_heads
+    for _ in range(samples):
+        b = int(rng.integers(0, spec.batch))
+        h = int(rng.integers(0, spec.num_q_heads))
+        L = int(lay.seq_lens[b])
+        rows = db.req_to_token[b, :L].long()
+        g = h // G
+        K = host(db.k_pools[0][rows, g:g + 1])
+        V = host(db.v_pools[0][rows, g:g + 1])
+        q = host(db.q[b:b + 1, h:h + 1])
+        ro, rl = oracle.paged_attention(q, K, V, np.arange(L)[None], [L], [0, 1])
+        assert_bf16_close(host(out[b:b + 1, h:h + 1]), ro, f"{name} b={b} h={h}")
+        assert abs(float(lse[b, h]) - rl[0, 0]) <= 2e-3
+
+
+def test_full_size_decode_bf16_sampled():
+    _sampled_full_size("decode_bf16", samples=24)
+
+
+def test_full_size_long_decode_sampled():
+    _sampled_full_size("long_decode_bf16", samples=6)

@@ -290,3 +290,88 @@ def permute_pages(layout: Layout, rng: np.random.Generator) -> Tuple[Layout, np.
                   new_slots=slot_map[layout.new_slots].astype(np.int32),
                   slot_owner=owner, slot_pos=pos)
     return new, slot_map
+
+
+# ---------------------------------------------------------------- device-side batches
+@dataclass
+class DeviceBatch:
+    """A batch whose integer structure comes from :func:`make_layout` and whose
+    values are drawn on the GPU with a seeded torch generator (for sizes where
+    host generation would be slow).  One set of pools per layer."""
+
+    layout: Layout
+    q: "object"  # [T, Hq, d] bf16 (fp8: uint8 E4M3 codes)
+    k_pools: list  # per layer [slots, Hkv, d]
+    v_pools: list
+    k_new: list  # per layer [T, Hkv, d]
+    v_new: list
+    req_to_token: "object"  # int32 [B, stride]
+    seq_lens: "object"  # int32 [B]
+    cu_seqlens_q: "object"  # int32 [B+1]
+    new_slots: "object"  # int32 [T]
+    sfq: "object" = None
+    sfk: "object" = None
+    sfv: "object" = None
+
+
+def _torch_seed(spec: Spec, seed: int) -> int:
+    return int(np.random.SeedSequence(seed_sequence(spec, seed)).generate_state(1)[0])
+
+
+def make_device_batch(spec: Spec, seed: int = 0, device="cuda", layers: int = 1,
+                      stride: Optional[int] = None) -> DeviceBatch:
+    """Draw lengths and the page table on the host, values on ``device``.
+
+    Draw order on the device: Q, then per layer the K pool and the V pool;
+    for fp8 the scales are drawn first on the host (U[lo, hi]) and the codes
+    are E4M3 casts of N(0,1)/scale.
+    """
+    import torch
+    lay, rng = make_layout(spec, seed, stride=stride)
+    T, Hq, Hkv, d = lay.total_q, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    S = lay.pool_slots
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(spec, seed))
+    dev = torch.device(device)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    new_slots = i32(lay.new_slots)
+    db = DeviceBatch(layout=lay, q=None, k_pools=[], v_pools=[], k_new=[], v_new=[],
+                     req_to_token=i32(lay.req_to_token), seq_lens=i32(lay.seq_lens),
+                     cu_seqlens_q=i32(lay.cu_seqlens_q), new_slots=new_slots)
+    if spec.dtype == "fp8":
+        B = spec.batch
+        lo, hi = spec.scale_range
+        nblk = max((lay.max_kv_len + spec.k_block - 1) // spec.k_block, 1)
+        sfq = rng.uniform(lo, hi, size=(B, Hq)).astype(np.float32)
+        sfk = rng.uniform(lo, hi, size=(B, Hkv, nblk)).astype(np.float32)
+        sfv = rng.uniform(lo, hi, size=(B, Hkv, d)).astype(np.float32)
+        db.sfq, db.sfk, db.sfv = (torch.from_numpy(x).to(dev) for x in (sfq, sfk, sfv))
+        used = lay.slot_owner >= 0
+        owner = torch.from_numpy(np.where(used, lay.slot_owner, 0).astype(np.int64)).to(dev)
+        blk = torch.from_numpy((np.where(used, lay.slot_pos, 0) // spec.k_block).astype(np.int64)).to(dev)
+        k_scale = db.sfk[owner, :, blk]  # [S, Hkv]
+        v_scale = db.sfv[owner]  # [S, Hkv, d]
+        req_of_row = torch.from_numpy(np.repeat(np.arange(B), lay.new_lens)).to(dev)
+        qf = torch.randn((T, Hq, d), generator=g, device=dev, dtype=torch.float32)
+        db.q = (qf / db.sfq[req_of_row][:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        for _ in range(layers):
+            kf = torch.randn((S, Hkv, d), generator=g, device=dev, dtype=torch.float32)
+            kc = (kf / k_scale[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+            del kf
+            vf = torch.randn((S, Hkv, d), generator=g, device=dev, dtype=torch.float32)
+            vc = (vf / v_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+            del vf
+            db.k_pools.append(kc)
+            db.v_pools.append(vc)
+            db.k_new.append(kc[new_slots.long()].contiguous())
+            db.v_new.append(vc[new_slots.long()].contiguous())
+        return db
+    db.q = torch.randn((T, Hq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    for _ in range(layers):
+        kp = torch.randn((S, Hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        vp = torch.randn((S, Hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        db.k_pools.append(kp)
+        db.v_pools.append(vp)
+        db.k_new.append(kp[new_slots.long()].contiguous())
+        db.v_new.append(vp[new_slots.long()].contiguous())
+    return db
