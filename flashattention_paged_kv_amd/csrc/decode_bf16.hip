@@ -19,7 +19,8 @@
 //
 // Items with one split write bf16 O and lse directly; otherwise the split's
 // normalised partial O and log2-sum-exp go to scratch and the merge kernel
-// combines them (log-sum-exp algebra, fixed order, deterministic).
+// (decode_merge.h) combines them.
+#include "decode_merge.h"
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -114,15 +115,19 @@ __device__ __forceinline__ void compute_tile(const KVTile<D>& t, const u32x4 (&q
 
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(DecodeArgs a) {
+// WPB waves per workgroup take WPB consecutive (kv head, head group) units of
+// the same split, so the rows of one token are requested together.
+template <int D, int WPB>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int KB = D / 32;
   const int32_t* __restrict__ ws = a.ws;
   if ((int)blockIdx.x >= ws[WS_NUM_ITEMS]) return;
+  const int unit = blockIdx.y * WPB + (threadIdx.x >> 6);
+  if (unit >= a.hkv * a.head_groups) return;
   const int4 it = reinterpret_cast<const int4*>(ws + a.items_off)[blockIdx.x];
   const int b = it.x, kv_begin = it.y, kv_end = it.z, part = it.w;
-  const int g = blockIdx.y / a.head_groups, hg = blockIdx.y - g * a.head_groups;
-  const int lane = threadIdx.x;
+  const int g = unit / a.head_groups, hg = unit - g * a.head_groups;
+  const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, j = lane >> 4;
   const int hl = hg * 16 + l16;
   const bool head_ok = hl < a.group;
@@ -162,12 +167,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
   float l = lpart + __shfl_xor(lpart, 16);
   l += __shfl_xor(l, 32);
-  if (!head_ok) return;
   const bool rows_ok = (D == 128) || (j < 2);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const float lse2 = l > 0.f ? m + __log2f(l) : kNegInf;
   if (part < 0) {
-    if (rows_ok) {
+    if (head_ok && rows_ok) {
       uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.hq + h) * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -177,62 +181,45 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         stg16(orow + 32 * j + 8 * r, w);
       }
     }
-    if (j == 0 && a.lse) a.lse[(int64_t)b * a.hq + h] = lse2 * kLn2;
-  } else {
-    if (rows_ok) {
-      float* po = a.part_o + ((int64_t)part * a.hq + h) * D;
+    if (head_ok && j == 0 && a.lse) a.lse[(int64_t)b * a.hq + h] = lse2 * kLn2;
+    return;
+  }
+  if (head_ok && rows_ok) {
+    float* po = a.part_o + ((int64_t)part * a.hq + h) * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        floatx4 w0 = {acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
-        floatx4 w1 = {acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv};
-        *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r) = w0;
-        *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r + 4) = w1;
-      }
+    for (int r = 0; r < 4; ++r) {
+      floatx4 w0 = {acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
+      floatx4 w1 = {acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv};
+      *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r) = w0;
+      *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r + 4) = w1;
     }
-    if (j == 0) a.part_lse[(int64_t)part * a.hq + h] = lse2;
   }
-}
-
-// Combine the split partials of requests with more than one split:
-// lse = log Σ_s exp(lse_s), O = Σ_s exp(lse_s - lse)·O_s (partials in log2 units).
-template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
-  const int b = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-  const int32_t* __restrict__ req = a.ws + a.req_off;
-  const int s0 = req[b];
-  int s1 = req[b + 1];
-  const int num = a.ws[WS_NUM_ITEMS];
-  s1 = s1 < num ? s1 : num;
-  if (s1 - s0 <= 1) return;
-  float M = kNegInf;
-  for (int s = s0; s < s1; ++s) M = fmaxf(M, a.part_lse[(int64_t)s * a.hq + h]);
-  float tot = 0.f, o = 0.f;
-  for (int s = s0; s < s1; ++s) {
-    const float ls = a.part_lse[(int64_t)s * a.hq + h];
-    const float w = ls == kNegInf ? 0.f : exp2_fast(ls - M);
-    tot += w;
-    o += w * a.part_o[((int64_t)s * a.hq + h) * D + d];
-  }
-  const float res = tot > 0.f ? o / tot : 0.f;
-  uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.hq + h) * D;
-  orow[d] = (uint16_t)(pack_bf16x2(res, 0.f) & 0xffffu);
-  if (d == 0 && a.lse) a.lse[(int64_t)b * a.hq + h] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : kNegInf;
-}
-
-hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
-                              hipStream_t s) {
-  if (capacity <= 0 || batch <= 0) return hipSuccess;
-  dim3 grid((unsigned)capacity, (unsigned)(a.hkv * a.head_groups));
-  if (head_dim == 128) hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, dim3(64), 0, s, a);
-  return hipGetLastError();
+  if (head_ok && j == 0) a.part_lse[(int64_t)part * a.hq + h] = lse2;
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int32_t batch, hipStream_t s) {
   if (batch <= 0) return hipSuccess;
   dim3 grid((unsigned)batch, (unsigned)a.hq);
-  if (head_dim == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(128), 0, s, a);
-  else hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(64), 0, s, a);
+  if (head_dim == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(kMergeThreads), 0, s, a);
+  else hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(kMergeThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
+                              hipStream_t s) {
+  if (capacity <= 0 || batch <= 0) return hipSuccess;
+  // up to 8 waves per workgroup: the kv heads of one split run side by side
+  const int units = a.hkv * a.head_groups;
+  const int wpb = units >= 8 ? 8 : (units >= 4 ? 4 : (units >= 2 ? 2 : 1));
+  dim3 grid((unsigned)capacity, (unsigned)ceil_div(units, wpb));
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * wpb), 0, s, a); };
+  if (head_dim == 128) {
+    if (wpb == 8) go(decode_bf16_kernel<128, 8>); else if (wpb == 4) go(decode_bf16_kernel<128, 4>);
+    else if (wpb == 2) go(decode_bf16_kernel<128, 2>); else go(decode_bf16_kernel<128, 1>);
+  } else {
+    if (wpb == 8) go(decode_bf16_kernel<64, 8>); else if (wpb == 4) go(decode_bf16_kernel<64, 4>);
+    else if (wpb == 2) go(decode_bf16_kernel<64, 2>); else go(decode_bf16_kernel<64, 1>);
+  }
   return hipGetLastError();
 }
 

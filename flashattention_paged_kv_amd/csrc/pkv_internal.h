@@ -36,7 +36,7 @@ struct WsLayout {
   int64_t req_off = WS_HEADER_INTS;  // [B+1] split / tile offsets
   int64_t items_off = 0;             // [cap][4] work items
   int64_t tmp_off = 0;               // extend: unsorted items [cap][4]
-  int64_t keys_off = 0;              // extend: u64 sort keys [pow2(cap)] (8-byte aligned)
+  int64_t keys_off = 0;              // u64 sort keys [pow2(cap)] (8-byte aligned)
   int64_t total_ints = 0;
   int64_t capacity = 0;
 };
@@ -45,6 +45,11 @@ inline int64_t next_pow2(int64_t x) {
   int64_t p = 1;
   while (p < x) p <<= 1;
   return p;
+}
+
+// Decode work units per split: one per (kv head, group of up to 16 query heads).
+inline int64_t decode_units(const pkv_params& p) {
+  return (int64_t)p.num_kv_heads * ceil_div(p.num_q_heads / p.num_kv_heads, 16);
 }
 
 inline int64_t decode_capacity(const pkv_params& p, int64_t batch) {
@@ -76,15 +81,10 @@ inline WsLayout ws_layout(const pkv_params& p, int mode, int64_t batch, int64_t 
   WsLayout w;
   w.req_off = WS_HEADER_INTS;
   w.items_off = align_up(w.req_off + batch + 1, 4);
-  if (mode == PKV_DECODE) {
-    w.capacity = decode_capacity(p, batch);
-    w.total_ints = w.items_off + 4 * w.capacity;
-  } else {
-    w.capacity = extend_capacity(p, batch, total_q);
-    w.tmp_off = w.items_off + 4 * w.capacity;
-    w.keys_off = align_up(w.tmp_off + 4 * w.capacity, 2);
-    w.total_ints = w.keys_off + 2 * next_pow2(w.capacity > 0 ? w.capacity : 1);
-  }
+  w.capacity = mode == PKV_DECODE ? decode_capacity(p, batch) : extend_capacity(p, batch, total_q);
+  w.tmp_off = w.items_off + 4 * w.capacity;
+  w.keys_off = align_up(w.tmp_off + 4 * w.capacity, 2);
+  w.total_ints = w.keys_off + 2 * next_pow2(w.capacity > 0 ? w.capacity : 1);
   return w;
 }
 

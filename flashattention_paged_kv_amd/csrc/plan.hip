@@ -4,9 +4,9 @@
 // as the sglang get_scheduler_metadata analysis describes (intro, code §1-3).
 //
 // One workgroup of 1024 threads: block reductions / scans over the requests,
-// then an item table written in parallel.  Extend items are sorted by causal
-// range (longest first) with a bitonic sort, in LDS up to kPlanLdsSortMax
-// items and in the workspace's key area beyond that.
+// then an item table written in parallel and ordered longest-first (decode:
+// by split length; extend: by causal KV range) with a bitonic sort, in LDS up
+// to kPlanLdsSortMax items and in the workspace's key area beyond that.
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -60,6 +60,10 @@ __device__ __forceinline__ int find_request(const int32_t* req, int batch, int64
     if (req[mid] <= i) lo = mid; else hi = mid;
   }
   return lo;
+}
+
+__device__ __forceinline__ int sort_size(int64_t num) {
+  return (int)(num <= 1 ? 1 : (1ll << (64 - __builtin_clzll((unsigned long long)(num - 1)))));
 }
 
 template <typename Ptr>
@@ -125,18 +129,36 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int64_t num = carry < a.capacity ? carry : a.capacity;
     __threadfence_block();
     __syncthreads();
-    // 3. items, request-major; the partial index of a split is its item index
-    for (int64_t i = threadIdx.x; i < num; i += blockDim.x) {
-      int b = find_request(req, B, i);
-      int s = (int)(i - req[b]);
-      int n = req[b + 1] - req[b];
-      int L = clamp_len(a.seq_lens[b], a.max_kv_len);
-      int tiles = (L + kDecodeTile - 1) / kDecodeTile;
-      int t0 = (int)(((int64_t)s * tiles) / n);
-      int t1 = (int)(((int64_t)(s + 1) * tiles) / n);
-      int kb = t0 * kDecodeTile;
-      int ke = t1 * kDecodeTile < L ? t1 * kDecodeTile : L;
-      items[i] = make_int4(b, kb, ke, n > 1 ? (int)i : -1);
+    // 3. items (b, kv_begin, kv_end, partial index), created request-major;
+    //    the partial index of split s of request b is req[b] + s
+    int4* tmp = reinterpret_cast<int4*>(ws + a.tmp_off);
+    const int n2 = sort_size(num);
+    const bool in_lds = n2 <= kPlanLdsSortMax;
+    uint64_t* keys_g = reinterpret_cast<uint64_t*>(ws + a.keys_off);
+    for (int64_t i = threadIdx.x; i < n2; i += blockDim.x) {
+      uint64_t key = ~0ull;
+      if (i < num) {
+        int b = find_request(req, B, i);
+        int s = (int)(i - req[b]);
+        int n = req[b + 1] - req[b];
+        int L = clamp_len(a.seq_lens[b], a.max_kv_len);
+        int tiles = (L + kDecodeTile - 1) / kDecodeTile;
+        int t0 = (int)(((int64_t)s * tiles) / n);
+        int t1 = (int)(((int64_t)(s + 1) * tiles) / n);
+        int kb = t0 * kDecodeTile;
+        int ke = t1 * kDecodeTile < L ? t1 * kDecodeTile : L;
+        tmp[i] = make_int4(b, kb, ke, n > 1 ? (int)i : -1);
+        key = ((uint64_t)(uint32_t)(0x7fffffff - (ke - kb)) << 32) | (uint64_t)i;  // longest split first
+      }
+      if (in_lds) keys_lds[i] = key; else keys_g[i] = key;
+    }
+    __threadfence_block();
+    __syncthreads();
+    if (in_lds) bitonic_sort_u64(keys_lds, n2);
+    else bitonic_sort_u64(keys_g, n2);
+    for (int64_t j = threadIdx.x; j < num; j += blockDim.x) {
+      uint64_t key = in_lds ? keys_lds[j] : keys_g[j];
+      items[j] = tmp[(uint32_t)(key & 0xffffffffu)];
     }
     if (threadIdx.x == 0) {
       ws[WS_MODE] = PKV_DECODE;
@@ -169,7 +191,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __threadfence_block();
   __syncthreads();
   int4* tmp = reinterpret_cast<int4*>(ws + a.tmp_off);
-  const int n2 = (int)(num <= 1 ? 1 : (1ll << (64 - __builtin_clzll((unsigned long long)(num - 1)))));
+  const int n2 = sort_size(num);
   const bool in_lds = n2 <= kPlanLdsSortMax;
   uint64_t* keys_g = reinterpret_cast<uint64_t*>(ws + a.keys_off);
   for (int64_t i = threadIdx.x; i < n2; i += blockDim.x) {

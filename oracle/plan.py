@@ -19,9 +19,11 @@ Decode rule (tile = 32 tokens):
 * splits_b = max(1, ceil(tiles_b / chunk_tiles)); split s covers tiles
   [⌊s·tiles_b/splits_b⌋, ⌊(s+1)·tiles_b/splits_b⌋), i.e. tokens
   [32·t0, min(32·t1, L_b)) (balanced, interior bounds on tile multiples).
-* items are listed request-major (b, s); a request with one split writes its
-  output directly (part index -1), otherwise split s of request b owns
-  partial slot split_off[b] + s with split_off the exclusive prefix sum.
+* items are created request-major (b, s); a request with one split writes
+  its output directly (part index -1), otherwise split s of request b owns
+  partial slot split_off[b] + s with split_off the exclusive prefix sum;
+  the list is then ordered by split length (tokens) descending, ties by
+  creation order (longest first, so the short splits fill the tail).
 * capacity (host-visible, never exceeded):
   automatic: min(target_splits + B, B · max(1, ceil(max_kv_len / 32)));
   fixed: B · max(1, ceil(max_kv_len / kv_chunk)).
@@ -85,6 +87,8 @@ def plan_decode(seq_lens, num_kv_heads: int, group: int, max_kv_len: int,
             ke = min(t1 * DECODE_TILE, int(L[b]))
             part = split_off[b] + s if splits[b] > 1 else -1
             items.append((b, kb, ke, part))
+    order = sorted(range(len(items)), key=lambda i: (-(items[i][2] - items[i][1]), i))
+    items = [items[i] for i in order]
     cap = decode_capacity(B, num_kv_heads, group, max_kv_len, kv_chunk, split_target)
     return {"chunk_tiles": chunk, "splits": np.array(splits, np.int64),
             "split_off": np.array(split_off, np.int64),

@@ -109,8 +109,11 @@ def test_decode_plan_invariants(seed, kv_chunk):
     assert len(items) <= plan["capacity"]
     Lc = np.minimum(L, max_kv)
     parts = []
+    lengths = items[:, 2] - items[:, 1]
+    assert np.all(np.diff(lengths) <= 0)  # longest split first
     for b in range(B):
         mine = items[items[:, 0] == b]
+        mine = mine[np.argsort(mine[:, 1], kind="stable")]
         assert len(mine) == plan["splits"][b] >= 1
         assert mine[0, 1] == 0 and mine[-1, 2] == Lc[b]
         assert np.all(mine[1:, 1] == mine[:-1, 2])  # contiguous, in order
@@ -120,11 +123,11 @@ def test_decode_plan_invariants(seed, kv_chunk):
         if len(mine) == 1:
             assert mine[0, 3] == -1
         else:
+            assert list(mine[:, 3]) == list(range(plan["split_off"][b], plan["split_off"][b + 1]))
             parts += list(mine[:, 3])
         if kv_chunk:
             assert np.all(mine[:, 2] - mine[:, 1] <= kv_chunk)
     assert sorted(parts) == sorted(set(parts))
-    assert np.all(np.diff(items[:, 0]) >= 0)
 
 
 @pytest.mark.parametrize("seed", range(4))
