@@ -167,6 +167,16 @@ def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan:
     B = seq_lens.shape[0]
     if plan.mode != PKV_DECODE or plan.batch != B:
         raise ValueError("plan was not made by plan_metadata(PKV_DECODE) for this batch")
+    if params.kv_dtype == PKV_FP8_E4M3 and sfk is not None:
+        nblk = -(-params.max_kv_len // params.k_block)
+        if tuple(sfk.shape) != (B, params.num_kv_heads, nblk):
+            raise ValueError(f"sfk must be [B, Hkv, ceil(max_kv_len/k_block)] = {(B, params.num_kv_heads, nblk)}")
+        if sfq is None or tuple(sfq.shape) != (B, params.num_q_heads):
+            raise ValueError("sfq must be [B, Hq]")
+        if sfv is None or tuple(sfv.shape) != (B, params.num_kv_heads, params.head_dim):
+            raise ValueError("sfv must be [B, Hkv, d]")
+        if v_mean is not None and tuple(v_mean.shape) != (B, params.num_kv_heads, params.head_dim):
+            raise ValueError("v_mean must be [B, Hkv, d]")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, 3)

@@ -1,5 +1,246 @@
+// 8-bit (OCP E4M3) split-KV decode following the Sage formula of the
+// FlashInfer PrimTS Sage page (code §1, §4):
+//
+//   S = sm_scale · sfQ[b,h] · sfK[b,g,⌊j/k_block⌋] · (q8 · k8_j)
+//   P8 = E4M3(448 · exp(S - m)),  l = Σ exp(S - m)  (unquantised)
+//   O = sfV[b,g,:] · (Σ_j P8_j · v8_j) / (448 · l)  (+ v_mean[b,g,:])
+//
+// Q and K scales enter before the row max and the exponential; the V scale
+// is per channel and applied once at the end.  This kernel keeps a running
+// max m (online softmax), so P8 is quantised against the running max and
+// the accumulator is rescaled in fp32 when the max grows.
+//
+// Same decomposition as the bf16 decode (one wave per (request, split, kv
+// head, 16-head group); a request with several splits is merged by
+// decode_merge_kernel), with 64-token tiles and the gfx950 fp8 MFMA
+// 16x16x128 (f8f6f4, unit block scales):
+//  * Sᵀ = K8·Q8ᵀ: one MFMA per 16 keys covers all 128 channels (each lane
+//    holds 32 bytes of one key row);
+//  * Oᵀ += V8ᵀ·P8ᵀ: each lane gathers 16 keys x 8 channels of V8 and
+//    transposes the bytes with permutes into 8 A operands; 64 of the 128
+//    k slots carry the tile's keys, the rest are zero.
 #include "device_common.h"
 #include "pkv_internal.h"
+
 namespace pkv {
-hipError_t launch_decode_fp8(const DecodeArgs&, int, int64_t, int32_t, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+constexpr int kTile8 = 64;
+
+__device__ __forceinline__ floatx4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, floatx4 c) {
+  // fp8 E4M3 for both operands (format 0), block scales 2^0 (E8M0 127)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+
+struct Tile8 {
+  u32x4 k[4][2];  // A operands of Sᵀ: 4 blocks of 16 keys, 32 bytes (channels 32j..32j+31)
+  u32x2 v[16];    // the lane's 16 V rows, channels 8*(lane%16) .. +8
+};
+
+// token (within the tile) of element e (0..15) held by lane group j in the Pᵀ / Vᵀ operands
+__device__ __forceinline__ int tok_of(int j, int e) { return 16 * (e >> 2) + 4 * j + (e & 3); }
+
+__device__ __forceinline__ int slot_at(const int32_t* __restrict__ rtt_row, int tok, int kv_end, int64_t pool_slots) {
+  return tok < kv_end ? clamp_slot(rtt_row[tok], pool_slots) : -1;
+}
+
+__device__ __forceinline__ void load_tile8(Tile8& t, int slot_a, int slot_b, const uint8_t* __restrict__ kbase,
+                                           const uint8_t* __restrict__ vbase, int64_t row_bytes, int lane) {
+  // slot_a: slot of token (lane & 63) of the tile, i.e. lanes hold tokens 0..63
+  const int l16 = lane & 15, j = lane >> 4;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  const u32x2 z2 = {0u, 0u};
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const int sk = __shfl(slot_a, 16 * blk + l16);
+    const uint8_t* p = kbase + (int64_t)sk * row_bytes + 32 * j;
+    t.k[blk][0] = sk >= 0 ? ldg16(p) : z4;
+    t.k[blk][1] = sk >= 0 ? ldg16(p + 16) : z4;
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int sv = __shfl(slot_a, tok_of(j, e));
+    t.v[e] = sv >= 0 ? ldg8(vbase + (int64_t)sv * row_bytes + 8 * l16) : z2;
+  }
+  (void)slot_b;
+}
+
+// 4x4 byte transpose: out[c] = {x0.byte c, x1.byte c, x2.byte c, x3.byte c}
+__device__ __forceinline__ void transpose4x4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t (&o)[4]) {
+  const uint32_t a_lo = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
+  const uint32_t a_hi = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
+  const uint32_t b_lo = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+  const uint32_t b_hi = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u);  // x0.b0 x1.b0 x2.b0 x3.b0
+  o[1] = __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u);
+}
+
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);  // bytes 0,1 (OCP E4M3, nearest even)
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);       // bytes 2,3
+  return (uint32_t)w;
+}
+
+}  // namespace
+
+template <int WPB>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_fp8_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  const int32_t* __restrict__ ws = a.ws;
+  if ((int)blockIdx.x >= ws[WS_NUM_ITEMS]) return;
+  const int unit = blockIdx.y * WPB + (threadIdx.x >> 6);
+  if (unit >= a.hkv * a.head_groups) return;
+  const int4 it = reinterpret_cast<const int4*>(ws + a.items_off)[blockIdx.x];
+  const int b = it.x, kv_begin = it.y, kv_end = it.z, part = it.w;
+  const int g = unit / a.head_groups, hg = unit - g * a.head_groups;
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, j = lane >> 4;
+  const int hl = hg * 16 + l16;
+  const bool head_ok = hl < a.group;
+  const int h = g * a.group + (head_ok ? hl : 0);
+  const int row = a.rpi ? a.rpi[b] : b;
+  const int32_t* __restrict__ rtt_row = a.rtt + (int64_t)row * a.rtt_stride;
+  const int64_t row_bytes = (int64_t)a.hkv * D;
+  const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k_pool) + (int64_t)g * D;
+  const uint8_t* __restrict__ vbase = static_cast<const uint8_t*>(a.v_pool) + (int64_t)g * D;
+  const float* __restrict__ sfk_row = a.sfk + ((int64_t)b * a.hkv + g) * a.sfk_stride;
+
+  // Q8 as the B operand: lane holds q8[h][32 j .. 32 j + 32]
+  i32x8 qop;
+  {
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + ((int64_t)b * a.hq + h) * D + 32 * j;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 q0 = head_ok ? ldg16(qrow) : z, q1 = head_ok ? ldg16(qrow + 16) : z;
+    qop = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3], (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
+  }
+  const float qscale = head_ok ? a.sfq[(int64_t)b * a.hq + h] * a.scale_log2 : 0.f;
+
+  float m = kNegInf, lpart = 0.f;
+  floatx4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (kv_begin < kv_end) {
+    Tile8 cur, nxt;
+    int slot_n = slot_at(rtt_row, kv_begin + lane, kv_end, a.pool_slots);
+    load_tile8(cur, slot_n, 0, kbase, vbase, row_bytes, lane);
+    slot_n = slot_at(rtt_row, kv_begin + kTile8 + lane, kv_end, a.pool_slots);
+    for (int t0 = kv_begin; t0 < kv_end; t0 += kTile8) {
+      const int slot_nn = slot_at(rtt_row, t0 + 2 * kTile8 + lane, kv_end, a.pool_slots);
+      load_tile8(nxt, slot_n, 0, kbase, vbase, row_bytes, lane);
+      // ---- scores: 4 blocks of 16 keys; every 16-key block lies in one sfK block
+      float sc[16];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const i32x8 kop = {(int)cur.k[blk][0][0], (int)cur.k[blk][0][1], (int)cur.k[blk][0][2], (int)cur.k[blk][0][3],
+                           (int)cur.k[blk][1][0], (int)cur.k[blk][1][1], (int)cur.k[blk][1][2], (int)cur.k[blk][1][3]};
+        floatx4 s = {0.f, 0.f, 0.f, 0.f};
+        s = mfma_fp8_16x16x128(kop, qop, s);
+        const int tb = t0 + 16 * blk;
+        const float ks = tb < kv_end ? sfk_row[tb / a.k_block] * qscale : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[4 * blk + r] = (tb + 4 * j + r < kv_end) ? s[r] * ks : kNegInf;
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);  // finite: key t0 is in range
+      const float alpha = exp2_fast(m - m_new);
+      m = m_new;
+      float p[16];
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p[e] = exp2_fast(sc[e] - m_new);
+        ps += p[e];
+      }
+      lpart = lpart * alpha + ps;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+      // P8ᵀ operand: element e (byte e) <-> key tok_of(j, e); bytes 16..31 are zero
+      i32x8 pop;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        pop[w] = (int)pack_fp8x4(448.f * p[4 * w], 448.f * p[4 * w + 1], 448.f * p[4 * w + 2], 448.f * p[4 * w + 3]);
+      pop[4] = pop[5] = pop[6] = pop[7] = 0;
+      // V8ᵀ operands: block c holds channel 8*l16 + c of the lane's 16 keys
+      uint32_t vt[8][4];  // [channel c][key group of 4]
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint32_t o_lo[4], o_hi[4];
+        transpose4x4(cur.v[4 * q4][0], cur.v[4 * q4 + 1][0], cur.v[4 * q4 + 2][0], cur.v[4 * q4 + 3][0], o_lo);
+        transpose4x4(cur.v[4 * q4][1], cur.v[4 * q4 + 1][1], cur.v[4 * q4 + 2][1], cur.v[4 * q4 + 3][1], o_hi);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          vt[c][q4] = o_lo[c];
+          vt[4 + c][q4] = o_hi[c];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const i32x8 vop = {(int)vt[c][0], (int)vt[c][1], (int)vt[c][2], (int)vt[c][3], 0, 0, 0, 0};
+        acc[c] = mfma_fp8_16x16x128(vop, pop, acc[c]);
+      }
+      cur = nxt;
+      slot_n = slot_nn;
+    }
+  }
+
+  float l = lpart + __shfl_xor(lpart, 16);
+  l += __shfl_xor(l, 32);
+  // Oᵀ block c, row 4 j + r  <->  channel d = 8 (4 j + r) + c = 32 j + 8 r + c
+  const float inv = l > 0.f ? 1.f / (448.f * l) : 0.f;
+  const float lse2 = l > 0.f ? m + __log2f(l) : kNegInf;
+  const float* sfv = a.sfv + ((int64_t)b * a.hkv + g) * D;
+  const float* vmean = a.v_mean ? a.v_mean + ((int64_t)b * a.hkv + g) * D : nullptr;
+  float o[4][8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int d = 32 * j + 8 * r + c;
+      o[r][c] = acc[c][r] * inv * sfv[d] + (vmean ? vmean[d] : 0.f);
+    }
+  if (part < 0) {
+    if (head_ok) {
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.hq + h) * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(o[r][2 * k], o[r][2 * k + 1]);
+        stg16(orow + 32 * j + 8 * r, w);
+      }
+      if (j == 0 && a.lse) a.lse[(int64_t)b * a.hq + h] = lse2 * kLn2;
+    }
+    return;
+  }
+  if (head_ok) {
+    float* po = a.part_o + ((int64_t)part * a.hq + h) * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r) = floatx4{o[r][0], o[r][1], o[r][2], o[r][3]};
+      *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r + 4) = floatx4{o[r][4], o[r][5], o[r][6], o[r][7]};
+    }
+    if (j == 0) a.part_lse[(int64_t)part * a.hq + h] = lse2;
+  }
+}
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch, hipStream_t s) {
+  (void)head_dim;  // 128 only (validated by the host API)
+  if (capacity <= 0 || batch <= 0) return hipSuccess;
+  const int units = a.hkv * a.head_groups;
+  const int wpb = units >= 8 ? 8 : (units >= 4 ? 4 : (units >= 2 ? 2 : 1));
+  dim3 grid((unsigned)capacity, (unsigned)ceil_div(units, wpb));
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * wpb), 0, s, a); };
+  if (wpb == 8) go(decode_fp8_kernel<8>); else if (wpb == 4) go(decode_fp8_kernel<4>);
+  else if (wpb == 2) go(decode_fp8_kernel<2>); else go(decode_fp8_kernel<1>);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,112 @@
+"""GPU parity of the 8-bit (OCP E4M3) Sage decode against the fp64 oracle of the
+formula, through the C ABI via the ctypes binding."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import FP8_REL_L2, dev_f32, dev_i32, dev_u8, host, rel_l2, torch_mod
+from workloads import SPECS, Spec, make_device_batch, make_host_batch, pool_before_store
+
+pytestmark = pytest.mark.gpu
+
+
+def _pkv():
+    import flashattention_paged_kv_amd as pkv
+    return pkv
+
+
+def run_fp8(hb, kv_chunk=0, v_mean=None, sm_scale=None):
+    torch = torch_mod()
+    pkv = _pkv()
+    lay = hb.layout
+    spec = lay.spec
+    k_pool = dev_u8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F))
+    v_pool = dev_u8(pool_before_store(hb.v_codes, lay.new_slots, fill=0x7F))
+    params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                        max_kv_len=lay.req_to_token.shape[1], kv_dtype=pkv.PKV_FP8_E4M3,
+                        q_block=spec.q_block, k_block=spec.k_block, kv_chunk=kv_chunk)
+    seq, rtt = dev_i32(lay.seq_lens), dev_i32(lay.req_to_token)
+    plan = pkv.plan_metadata(params, pkv.PKV_DECODE, seq)
+    pkv.kv_store(params, k_pool, v_pool, dev_u8(hb.k_new_codes), dev_u8(hb.v_new_codes), dev_i32(lay.new_slots))
+    lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+    out = pkv.attn_decode(params, dev_u8(hb.q_codes), k_pool, v_pool, rtt, seq, plan, lse=lse, sm_scale=sm_scale,
+                          sfq=dev_f32(hb.sfq), sfk=dev_f32(hb.sfk), sfv=dev_f32(hb.sfv),
+                          v_mean=None if v_mean is None else dev_f32(v_mean))
+    torch.cuda.synchronize()
+    return host(out), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_fp8(hb, v_mean=None, sm_scale=None):
+    lay = hb.layout
+    return oracle.sage_decode(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens, hb.sfq, hb.sfk,
+                              hb.sfv, lay.spec.k_block, sm_scale=sm_scale, v_mean=v_mean)
+
+
+SMALL = Spec("f8_small", "decode", 6, 32, 8, 128, 16, (0, 700), 1, dtype="fp8", k_block=64)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("k_block", [64, 16])
+def test_fp8_decode_matches_sage_oracle(seed, k_block):
+    from dataclasses import replace
+    hb = make_host_batch(replace(SMALL, k_block=k_block), seed)
+    o, lse = run_fp8(hb)
+    ro, rlse = oracle_fp8(hb)
+    assert np.all(np.isfinite(o))
+    rel = rel_l2(o, ro)
+    assert rel <= FP8_REL_L2, rel
+    assert np.abs(lse - rlse).max() <= 1e-3
+
+
+def test_fp8_split_merge_and_v_mean():
+    hb = make_host_batch(SMALL, 3)
+    vm = np.random.default_rng(0).uniform(-1, 1, size=hb.sfv.shape).astype(np.float32)
+    o1, l1 = run_fp8(hb, kv_chunk=64, v_mean=vm)
+    o2, l2 = run_fp8(hb, kv_chunk=4096, v_mean=vm)
+    ro, rlse = oracle_fp8(hb, v_mean=vm)
+    assert rel_l2(o1, ro) <= FP8_REL_L2 and rel_l2(o2, ro) <= FP8_REL_L2
+    assert np.abs(l1 - rlse).max() <= 1e-3
+
+
+def test_fp8_constant_scores_closed_form():
+    """q8 = 0: every p is 1, P8 = 448 exactly, so O = sfV * mean(V8) up to fp32 sums."""
+    hb = make_host_batch(SMALL, 4)
+    hb.q_codes[:] = 0
+    o, lse = run_fp8(hb)
+    ro, _ = oracle_fp8(hb)
+    lay = hb.layout
+    for b in range(SMALL.batch):
+        L = int(lay.seq_lens[b])
+        np.testing.assert_allclose(lse[b], np.log(L), rtol=0, atol=1e-5)
+    assert rel_l2(o, ro) <= 4e-3  # only bf16 output rounding and fp32 sums remain
+
+
+def test_full_size_fp8_decode_sampled():
+    torch = torch_mod()
+    pkv = _pkv()
+    spec = SPECS["decode_fp8"]
+    db = make_device_batch(spec, seed=0, layers=1)
+    lay = db.layout
+    params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                        max_kv_len=lay.req_to_token.shape[1], kv_dtype=pkv.PKV_FP8_E4M3,
+                        q_block=spec.q_block, k_block=spec.k_block)
+    plan = pkv.plan_metadata(params, pkv.PKV_DECODE, db.seq_lens)
+    pkv.kv_store(params, db.k_pools[0], db.v_pools[0], db.k_new[0], db.v_new[0], db.new_slots)
+    out = pkv.attn_decode(params, db.q, db.k_pools[0], db.v_pools[0], db.req_to_token, db.seq_lens, plan,
+                          sfq=db.sfq, sfk=db.sfk, sfv=db.sfv)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(0)
+    got, ref = [], []
+    for _ in range(24):
+        b = int(rng.integers(0, spec.batch))
+        L = int(lay.seq_lens[b])
+        rows = db.req_to_token[b, :L].long()
+        q8 = db.q[b:b + 1].cpu().numpy()
+        k8 = db.k_pools[0][rows].cpu().numpy()
+        v8 = db.v_pools[0][rows].cpu().numpy()
+        o, _ = oracle.sage_decode(q8, k8, v8, np.arange(L)[None], [L], db.sfq[b:b + 1].cpu().numpy(),
+                                  db.sfk[b:b + 1].cpu().numpy(), db.sfv[b:b + 1].cpu().numpy(), spec.k_block)
+        got.append(host(out[b:b + 1]))
+        ref.append(o)
+        assert rel_l2(got[-1], o) <= FP8_REL_L2, b
