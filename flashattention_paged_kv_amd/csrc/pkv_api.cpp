@@ -163,7 +163,7 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
   if (pool_slots < 1) return fail(PKV_EINVAL, "pool_slots=%lld must be >= 1", (long long)pool_slots);
   if (rtt_stride < params->max_kv_len)
     return fail(PKV_EINVAL, "rtt_stride=%lld is smaller than max_kv_len=%d", (long long)rtt_stride, params->max_kv_len);
-  if (!std::isfinite(sm_scale)) return fail(PKV_EINVAL, "sm_scale must be finite");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f)) return fail(PKV_EINVAL, "sm_scale must be finite and > 0");
   const bool fp8 = params->kv_dtype == PKV_FP8_E4M3;
   if (!fp8) {
     if (sfq) return fail(PKV_EINVAL, "sfq is unsupported by a bf16 plan");
@@ -234,7 +234,7 @@ int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void*
   if (pool_slots < 1) return fail(PKV_EINVAL, "pool_slots=%lld must be >= 1", (long long)pool_slots);
   if (rtt_stride < params->max_kv_len)
     return fail(PKV_EINVAL, "rtt_stride=%lld is smaller than max_kv_len=%d", (long long)rtt_stride, params->max_kv_len);
-  if (!std::isfinite(sm_scale)) return fail(PKV_EINVAL, "sm_scale must be finite");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f)) return fail(PKV_EINVAL, "sm_scale must be finite and > 0");
   if (batch == 0 || total_q == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !req_to_token || !seq_lens || !cu_seqlens_q || !workspace)
     return fail(PKV_EINVAL, "a required pointer (out, q, pools, req_to_token, seq_lens, cu_seqlens_q, workspace) is NULL");
