@@ -57,4 +57,13 @@ __device__ __forceinline__ int clamp_slot(int s, int64_t pool_slots) {
   return (uint32_t)s < (uint64_t)pool_slots ? s : (s < 0 ? 0 : (int)(pool_slots - 1));
 }
 
+// Cheaper clamp for hot loops: `last` = pool_slots - 1 (< 2^31); a negative
+// slot becomes a huge unsigned value and is clamped to the last row.
+__device__ __forceinline__ uint32_t clamp_slot_u32(int s, uint32_t last) { return min((uint32_t)s, last); }
+
+// Byte/element offset of a pool row: 32 x 32 -> 64-bit multiply.
+__device__ __forceinline__ int64_t row_offset(uint32_t slot, uint32_t row_elems) {
+  return (int64_t)((uint64_t)slot * (uint64_t)row_elems);
+}
+
 }  // namespace pkv

@@ -3,13 +3,22 @@
 //
 // The score matrix never leaves the chip (FlashAttention page, §2): a
 // workgroup walks the key range in 64-key tiles, gathers each K and V tile
-// through req_to_token into LDS (double buffered, staged through registers
-// one tile ahead), and keeps a running max / sum per row (online softmax).
+// through req_to_token into LDS and keeps a running max / sum per row
+// (online softmax).
 //
-// Work item = (request b, query tile t, kv head g).  Its 128 rows are the
+// Work item = (request b, query tile t, kv head g).  Its 256 rows are the
 // (query head, token) pairs of the G query heads that share kv head g, for
-// block = 128 / G consecutive new tokens (head-major rows), so every K/V byte
-// gathered into LDS serves all G heads.  Four waves own 32 rows each.
+// block = 256 / G consecutive new tokens (head-major rows), so every K/V byte
+// brought into LDS serves 256 rows.  Eight waves own 32 rows each; one
+// workgroup fills a CU (two waves per SIMD).
+//
+// Data movement is asynchronous and register-free: global -> LDS loads
+// (gfx950 global_load_lds_*) fill a ring of three K/V stages and four slot
+// stages.  While tile t is computed, the K/V rows of tile t+2 and the
+// req_to_token entries of tile t+3 are in flight; the slots of a tile are
+// read from LDS one step before its K/V rows are requested.  The tile loop is
+// unrolled by the ring period (3), so every LDS address is a per-lane offset
+// computed once plus an immediate.
 //
 // Per wave and key tile, with 32x32x16 bf16 MFMAs:
 //  * Sᵀ = K·Qᵀ: K rows from LDS are the A operand (16-byte reads), the
@@ -23,6 +32,8 @@
 //    output.
 // Causal mask (bottom-right aligned): row token i of a request with prefix
 // p sees keys 0..p+i; key tiles entirely above a wave's rows skip the MFMAs.
+#include <type_traits>
+
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -30,33 +41,54 @@ namespace pkv {
 
 namespace {
 
-constexpr int kBN = kExtendTileN;  // keys per tile (64)
-constexpr int kThreads = 256;      // 4 waves x 32 rows
+constexpr int kBN = kExtendTileN;         // keys per tile (64)
+constexpr int kWaves = kExtendRows / 32;  // 8 waves x 32 rows
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKVStages = 3;
+constexpr int kSlotStages = 3;  // same period as the K/V ring: stage indices are static
 
-// One stage holds a K tile and a V tile, rows of D*2 bytes, unpadded.  The
-// 16-byte chunk c of key row r sits at chunk position c ^ (r % CH): rows of
-// consecutive keys start on different banks, so 16-byte K row reads and the
-// 8-byte transpose reads of V are free of bank conflicts.
+// One K/V stage: a K tile then a V tile, rows of D*2 bytes, unpadded, with the
+// 16-byte chunks of each row XOR-swizzled against bank conflicts:
+//  * K: chunk c of key r at position c ^ (r % CH) -- the 16-byte row reads of
+//    the Sᵀ product touch one chunk of many consecutive keys;
+//  * V: chunk c of key r at position c ^ (2 (r % 8) % CH) -- each transpose
+//    read touches a 32-byte chunk pair of 4 consecutive keys, and XOR with an
+//    even value keeps pairs aligned while moving each key to another pair.
 template <int D>
 struct ExtSmem {
-  static constexpr int RB = D * 2;          // bytes per key row
-  static constexpr int CH = D / 8;          // 16-byte chunks per row
-  static constexpr int MAT = kBN * RB;      // one matrix tile
-  static constexpr int STAGE = 2 * MAT;     // K then V
-  static constexpr int ROWS_PER_KB = 1024 / RB;  // rows written by one 64-lane 16-byte load
+  static constexpr int RB = D * 2;                        // bytes per key row
+  static constexpr int CH = D / 8;                        // 16-byte chunks per row
+  static constexpr int MAT = kBN * RB;                    // one matrix tile
+  static constexpr int STAGE = 2 * MAT;                   // K then V
+  static constexpr int ROWS_PER_KB = 1024 / RB;           // rows written by one 64-lane 16-byte load
+  static constexpr int NQ = kBN / ROWS_PER_KB / kWaves;   // such loads per wave and matrix
+  static constexpr int SLOT_BYTES = kBN * 4;              // req_to_token entries of one tile
+  static constexpr int TOTAL = kKVStages * STAGE + kSlotStages * SLOT_BYTES;
 };
 
 template <int D>
-__device__ __forceinline__ int swz_off(int row, int chunk) {
-  return row * ExtSmem<D>::RB + ((chunk ^ (row & (ExtSmem<D>::CH - 1))) << 4);
+__device__ __forceinline__ int swz_k(int row) { return row & (ExtSmem<D>::CH - 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) { return (2 * (row & 7)) & (ExtSmem<D>::CH - 1); }
+template <int D>
+__device__ __forceinline__ int k_off(int row, int chunk) {
+  return row * ExtSmem<D>::RB + ((chunk ^ swz_k<D>(row)) << 4);
+}
+template <int D>
+__device__ __forceinline__ int v_off(int row, int chunk) {
+  return row * ExtSmem<D>::RB + ((chunk ^ swz_v<D>(row)) << 4);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(lds_char*)(const_cast<char*>(p));
+}
 
 __device__ __forceinline__ u32x2 lds_read_tr16(const char* base, uint32_t off) {
   // transposing 8-byte LDS read (gfx950): see the kernel header
-  typedef __attribute__((address_space(3))) char lds_char;
   lds_char* p = (lds_char*)(const_cast<char*>(base)) + off;
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(p));
   return __builtin_bit_cast(u32x2, v);
@@ -66,191 +98,196 @@ __device__ __forceinline__ floatx16 mfma32x32x16(bf16x8 a, bf16x8 b, floatx16 c)
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Full tiles go global -> LDS directly (gfx950 global_load_lds_dwordx4): each
-// 64-lane load writes 1 KiB of consecutive LDS, lane i at byte 16 i, i.e.
-// row i / CH, chunk position i % CH; the lane fetches the global chunk that
-// the swizzle puts there.  No registers, no LDS store instructions.
-template <int D>
-struct TileSlots {
-  static constexpr int NQ = kBN / ExtSmem<D>::ROWS_PER_KB / 4;  // 16-byte loads per lane per matrix
-  int s[NQ];  // raw req_to_token entries; -1 past kv_end (clamped when used)
-};
+// Global -> LDS loads.  Written as inline assembly so the compiler neither
+// counts them nor orders LDS reads of other stages behind them; the kernel
+// waits for them explicitly (wait_vmem<N>) before publishing a stage.  Each
+// 64-lane instruction writes consecutive LDS bytes from `lds` (M0), lane i at
+// lds + i * size.  M0 is used by nothing else in this kernel.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else static_assert(N == 0 || N == 2 || N == 4, "unsupported wait depth");
+}
 
 // Row of the tile handled by (wave, load q, lane); the lane writes LDS chunk
-// position lane % CH of that row and so fetches global chunk (lane % CH) ^ swizzle.
+// position lane % CH of that row and so fetches the global chunk the swizzle
+// puts there.
 template <int D>
 __device__ __forceinline__ int tile_row(int wave, int q, int lane) {
-  return (wave * TileSlots<D>::NQ + q) * ExtSmem<D>::ROWS_PER_KB + lane / ExtSmem<D>::CH;
+  return (wave * ExtSmem<D>::NQ + q) * ExtSmem<D>::ROWS_PER_KB + lane / ExtSmem<D>::CH;
 }
 
+// K and V rows of one tile into a stage, from the slots in a slot stage.
 template <int D>
-__device__ __forceinline__ int tile_chunk(int row, int lane) {
-  return (lane % ExtSmem<D>::CH) ^ (row & (ExtSmem<D>::CH - 1));
-}
-
-template <int D>
-__device__ __forceinline__ void load_tile_slots(TileSlots<D>& sl, const int32_t* __restrict__ rtt_row, int t0,
-                                                int kv_end, int wave, int lane) {
+__device__ __forceinline__ void issue_kv(const char* slots, char* stage, const uint16_t* __restrict__ kbase,
+                                         const uint16_t* __restrict__ vbase, uint32_t row_elems,
+                                         uint32_t last_slot, int wave, int lane) {
+  const int p = lane % ExtSmem<D>::CH;
 #pragma unroll
-  for (int q = 0; q < TileSlots<D>::NQ; ++q) {
-    const int key = t0 + tile_row<D>(wave, q, lane);
-    sl.s[q] = key < kv_end ? rtt_row[key] : -1;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void dma_tile(const TileSlots<D>& sl, char* stage, const uint16_t* __restrict__ kbase,
-                                         const uint16_t* __restrict__ vbase, int64_t row_elems, int64_t pool_slots,
-                                         int wave, int lane) {
-  typedef __attribute__((address_space(3))) void lds_void;
-#pragma unroll
-  for (int q = 0; q < TileSlots<D>::NQ; ++q) {
+  for (int q = 0; q < ExtSmem<D>::NQ; ++q) {
     const int r = tile_row<D>(wave, q, lane);
-    const int64_t slot = clamp_slot(sl.s[q], pool_slots);  // rows past kv_end read a valid row
-    const int64_t off = slot * row_elems + 8 * tile_chunk<D>(r, lane);
-    char* dst = stage + (wave * TileSlots<D>::NQ + q) * 1024;
-    __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)dst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(dst + ExtSmem<D>::MAT), 16, 0, 0);
+    const int s = *reinterpret_cast<const int*>(slots + 4 * r);
+    const int64_t row_off = row_offset(clamp_slot_u32(s, last_slot), row_elems);
+    const uint32_t dst = lds_addr(stage) + (wave * ExtSmem<D>::NQ + q) * 1024;
+    dma16(kbase + row_off + 8 * (p ^ swz_k<D>(r)), dst);
+    dma16(vbase + row_off + 8 * (p ^ swz_v<D>(r)), dst + ExtSmem<D>::MAT);
   }
 }
 
-// Rows past kv_end (only in a request's last, partial tile) are fetched from a
-// clamped slot and then overwritten with zeros by the wave that fetched them,
-// after its own loads have landed: a poisoned V row times a zero probability
-// would still be NaN.  Bit q of the mask marks load q of this lane as such a row.
-template <int D>
-__device__ __forceinline__ int invalid_mask(const TileSlots<D>& sl) {
-  int mask = 0;
-#pragma unroll
-  for (int q = 0; q < TileSlots<D>::NQ; ++q) mask |= (sl.s[q] < 0) << q;
-  return mask;
+// req_to_token entries of the 64 keys of a tile (one wave; keys past kv_end
+// read the last valid entry, their rows are zeroed later).
+__device__ __forceinline__ void issue_slots(const int32_t* __restrict__ rtt_row, int t0, int kv_end,
+                                            char* slot_stage, int lane) {
+  dma4(rtt_row + min(t0 + lane, kv_end - 1), lds_addr(slot_stage));
 }
 
+// Rows past kv_end that this lane fetched are overwritten with zeros once its
+// own loads have landed: a poisoned V row times a zero probability would
+// still be NaN.
 template <int D>
-__device__ __forceinline__ void zero_invalid_rows(int mask, char* stage, int wave, int lane) {
+__device__ __forceinline__ void zero_rows_past_end(char* stage, int t0, int kv_end, int wave, int lane) {
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int q = 0; q < TileSlots<D>::NQ; ++q)
-    if (mask & (1 << q)) {
-      char* dst = stage + (wave * TileSlots<D>::NQ + q) * 1024 + 16 * lane;
+  for (int q = 0; q < ExtSmem<D>::NQ; ++q) {
+    if (t0 + tile_row<D>(wave, q, lane) >= kv_end) {
+      char* dst = stage + (wave * ExtSmem<D>::NQ + q) * 1024 + 16 * lane;
       *reinterpret_cast<u32x4*>(dst) = z;
       *reinterpret_cast<u32x4*>(dst + ExtSmem<D>::MAT) = z;
     }
+  }
 }
 
-__device__ __forceinline__ void wait_vmem_all() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Per-lane LDS byte offsets of the Vᵀ transpose reads for each 32-channel block:
+// key 4 jj + i16/4 (its swizzle is the same for every 16-key step and +8), the
+// chunk pair of channel 32 db + dsub + 4 (i16 % 4); key steps are immediate offsets.
+template <int D>
+__device__ __forceinline__ void v_read_bases(int (&vb)[D / 32], int lane) {
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int key = 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+    vb[db] = v_off<D>(key, col >> 3) + ((col & 7) << 1);
+  }
+}
 
-}  // namespace
+// Per-lane LDS byte offsets of the K row reads of the Sᵀ product, one per
+// 16-channel k-step: key lane % 32 (key + 32 has the same swizzle), chunk 2 ks + jh.
+template <int D>
+__device__ __forceinline__ void k_read_offsets(int (&ko)[D / 16], int lane) {
+  const int key = lane & 31, jh = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) ko[ks] = k_off<D>(key, 2 * ks + jh);
+}
 
-// Per-row state and the compute of one key tile (Sᵀ, mask, online softmax, Oᵀ).
 template <int D>
 struct RowState {
   floatx16 acc[D / 32];
   float m, lpart;
 };
 
+// One key tile: Sᵀ, mask, online softmax, Oᵀ.  The two 32-key halves keep
+// their own softmax step, so the VALU work of one half runs while the matrix
+// cores work on the other: QK of both halves is issued first, the softmax of
+// half 0 overlaps QK of half 1, the softmax of half 1 overlaps PV of half 0.
 template <int D>
-__device__ __forceinline__ void compute_tile(RowState<D>& rs, const char* cur, const u32x4 (&qop)[D / 16], int t0,
+__device__ __forceinline__ void compute_tile(RowState<D>& rs, const char* cur, const u32x4 (&qop)[D / 16],
+                                             const int (&koff)[D / 16], const int (&vbase_off)[D / 32], int t0,
                                              int pos, int wave_min_pos, float c, int lane) {
   constexpr int QK_STEPS = D / 16;
   constexpr int DB = D / 32;
-  const int l32 = lane & 31, jh = lane >> 5;
+  const int jh = lane >> 5;
   // ---- Sᵀ for two 32-key blocks (raw scores; the scale is folded in below)
   floatx16 s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-    const int key = 32 * kb + l32;
 #pragma unroll
     for (int ks = 0; ks < QK_STEPS; ++ks) {
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(cur + swz_off<D>(key, 2 * ks + jh));
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(cur + 32 * kb * ExtSmem<D>::RB + koff[ks]);
       s[kb] = mfma32x32x16(as_bf16x8(kv), as_bf16x8(qop[ks]), s[kb]);
     }
   }
-  // ---- causal mask only where the tile crosses some row's diagonal
-  if (t0 + kBN - 1 > wave_min_pos) {
+  const bool masked = t0 + kBN - 1 > wave_min_pos;  // the tile crosses some row's diagonal
+  const char* vt = cur + ExtSmem<D>::MAT;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb) {
+    if (masked) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * jh + (r & 3);
         s[kb][r] = key <= pos ? s[kb][r] : kNegInf;
       }
-  }
-  float mx = kNegInf;
+    }
+    float mx = s[kb][0];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    // lazy rescale: the reference max moves only when a row's max exceeds it by
+    // more than 8 (log2 units), so exp2(s - m) <= 256 while acc and l keep
+    // referring to the same m
+    if (__any(mx > rs.m + 8.f)) {
+      const float m_new = fmaxf(rs.m, mx);
+      const float alpha = m_new == kNegInf ? 1.f : exp2_fast(rs.m - m_new);
+      rs.lpart *= alpha;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-  // ---- lazy rescale: the reference max moves only when a row's max exceeds it
-  //      by more than 8 (log2 units), so exp2(s - m) <= 256 while acc and l keep
-  //      referring to the same m
-  if (__any(mx > rs.m + 8.f)) {
-    const float m_new = fmaxf(rs.m, mx);
-    const float alpha = m_new == kNegInf ? 1.f : exp2_fast(rs.m - m_new);
-    rs.lpart *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) rs.acc[db] *= alpha;
-    rs.m = m_new;
-  }
-  const float m_use = rs.m == kNegInf ? 0.f : rs.m;
-  float ps = 0.f;
-  u32x4 pop[4];  // Pᵀ B operands, one per 16-key k-step
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+      for (int db = 0; db < DB; ++db) rs.acc[db] *= alpha;
+      rs.m = m_new;
+    }
+    const float m_use = rs.m == kNegInf ? 0.f : rs.m;
+    u32x4 pop[2];  // Pᵀ B operands of the half's two 16-key k-steps
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       float pv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = exp2_fast(__builtin_fmaf(s[kb][8 * half + e], c, -m_use));
-        ps += pv[e];
+      for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[kb][8 * half + e], c, -m_use));
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pop[half][w] = pack_bf16x2(pv[2 * w], pv[2 * w + 1]);
+        rs.lpart += pv[2 * w] + pv[2 * w + 1];
       }
-      u32x4 w;
-      w[0] = pack_bf16x2(pv[0], pv[1]);
-      w[1] = pack_bf16x2(pv[2], pv[3]);
-      w[2] = pack_bf16x2(pv[4], pv[5]);
-      w[3] = pack_bf16x2(pv[6], pv[7]);
-      pop[2 * kb + half] = w;
     }
-  rs.lpart += ps;
-  // ---- Oᵀ += Vᵀ·Pᵀ.  k-step ks2 covers keys 16 ks2 .. +16; this lane's 8 keys are
-  //      {16 ks2 + 8 (e/4) + 4 jh + e%4}: two transposed 4-key reads
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int dsub = 16 * (g16 & 1);
-  const int jj = g16 >> 1;
-  const char* vt = cur + ExtSmem<D>::MAT;
+    // Oᵀ += Vᵀ·Pᵀ.  k-step ks2 covers keys 16 ks2 .. +16; this lane's 8 keys are
+    // {16 ks2 + 8 (e/4) + 4 jh + e%4}: two transposed 4-key reads
 #pragma unroll
-  for (int ks2 = 0; ks2 < 4; ++ks2) {
-    const int key_a = 16 * ks2 + 4 * jj + (i16 >> 2);
-    const int key_b = key_a + 8;
+    for (int half = 0; half < 2; ++half) {
+      const int ks2 = 2 * kb + half;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int col = 32 * db + dsub + 4 * (i16 & 3);
-      const u32x2 va = lds_read_tr16(vt, swz_off<D>(key_a, col >> 3) + ((col & 7) << 1));
-      const u32x2 vb = lds_read_tr16(vt, swz_off<D>(key_b, col >> 3) + ((col & 7) << 1));
-      u32x4 vop = {va[0], va[1], vb[0], vb[1]};
-      rs.acc[db] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(pop[ks2]), rs.acc[db]);
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 va = lds_read_tr16(vt + 16 * ks2 * ExtSmem<D>::RB, vbase_off[db]);
+        const u32x2 vb = lds_read_tr16(vt + (16 * ks2 + 8) * ExtSmem<D>::RB, vbase_off[db]);
+        u32x4 vop = {va[0], va[1], vb[0], vb[1]};
+        rs.acc[db] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(pop[half]), rs.acc[db]);
+      }
     }
   }
 }
 
+}  // namespace
+
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void extend_bf16_kernel(ExtendArgs a) {
+  using S = ExtSmem<D>;
   constexpr int QK_STEPS = D / 16;  // k-steps of Sᵀ = K·Qᵀ
   constexpr int DB = D / 32;        // 32-channel blocks of Oᵀ
-  // two separate arrays, so the compiler can tell loads into one stage from reads of the other
-  __shared__ __attribute__((aligned(1024))) char smem0[ExtSmem<D>::STAGE];
-  __shared__ __attribute__((aligned(1024))) char smem1[ExtSmem<D>::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[S::TOTAL];
 
   const int32_t* __restrict__ ws = a.ws;
   if ((int)blockIdx.x >= ws[WS_NUM_ITEMS]) return;
   const int4 it = reinterpret_cast<const int4*>(ws + a.items_off)[blockIdx.x];
   const int b = it.x, qt = it.y, kv_end = it.z;
   const int g = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS targets on the scalar unit
   const int l32 = lane & 31, jh = lane >> 5;
 
   // request geometry, clamped exactly as the plan clamps it
@@ -284,11 +321,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ks = 0; ks < QK_STEPS; ++ks) qop[ks] = row_ok ? ldg16(qrow + 16 * ks + 8 * jh) : z;
+    // let the compiler see Q land here (vmcnt(0), other counters untouched), so
+    // it does not wait for "outstanding" loads inside the tile loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
   const int row_idx = a.rpi ? a.rpi[b] : b;
   const int32_t* __restrict__ rtt_row = a.rtt + (int64_t)row_idx * a.rtt_stride;
-  const int64_t row_elems = (int64_t)a.hkv * D;
+  const uint32_t row_elems = (uint32_t)(a.hkv * D);
+  const uint32_t last_slot = (uint32_t)(a.pool_slots - 1);
   const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * D;
   const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * D;
   const float c = a.scale_log2;  // > 0 (checked by the host API)
@@ -300,45 +341,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int r = 0; r < 16; ++r) rs.acc[db][r] = 0.f;
   rs.m = kNegInf;
   rs.lpart = 0.f;
+  int vbo[DB];
+  v_read_bases<D>(vbo, lane);
 
+  int ko[QK_STEPS];
+  k_read_offsets<D>(ko, lane);
+  char* const kv0 = smem;  // three K/V stages, then three slot stages
+  char* const slot0 = smem + kKVStages * S::STAGE;
   const int ntiles = (kv_end + kBN - 1) / kBN;
-  char* const stage0 = smem0;
-  char* const stage1 = smem1;
-  // two alternating slot sets: one feeds this step's loads, the other is refilled
-  TileSlots<D> sl_a, sl_b;
-  // tile 0 into stage 0, slots of tile 1 ahead
+
+  // prologue: slots of tiles 0..2 (wave 0), then K/V of tiles 0 and 1
   if (ntiles > 0) {
-    load_tile_slots<D>(sl_b, rtt_row, 0, kv_end, wave, lane);
-    load_tile_slots<D>(sl_a, rtt_row, kBN, kv_end, wave, lane);
-    dma_tile<D>(sl_b, stage0, kbase, vbase, row_elems, a.pool_slots, wave, lane);
-    const int bad = invalid_mask<D>(sl_b);
-    wait_vmem_all();
-    if (bad) zero_invalid_rows<D>(bad, stage0, wave, lane);
+    if (wave == 0) {
+      for (int t = 0; t < 3 && t < ntiles; ++t) issue_slots(rtt_row, t * kBN, kv_end, slot0 + t * S::SLOT_BYTES, lane);
+      wait_vmem<0>();
+    }
+    __syncthreads();
+    issue_kv<D>(slot0, kv0, kbase, vbase, row_elems, last_slot, wave, lane);
+    if (ntiles > 1) {
+      issue_kv<D>(slot0 + S::SLOT_BYTES, kv0 + S::STAGE, kbase, vbase, row_elems, last_slot, wave, lane);
+      wait_vmem<2 * S::NQ>();  // tile 0 lands, tile 1 may stay in flight
+    } else {
+      wait_vmem<0>();
+    }
+    zero_rows_past_end<D>(kv0, 0, kv_end, wave, lane);
   }
   __syncthreads();
 
-  // One step: prefetch tile t+1 into `nxt` (global -> LDS), compute tile t
-  // from `cur`, then publish tile t+1 to the workgroup.
-  auto step = [&](int tile, const char* cur, char* nxt, TileSlots<D>& use, TileSlots<D>& fill) {
+  // One step over tile `tile` whose ring index is J = tile % 3 (compile time).
+  auto step = [&](int tile, auto J_) {
+    constexpr int J = decltype(J_)::value;
+    constexpr int J1 = (J + 1) % 3, J2 = (J + 2) % 3;
     const int t0 = tile * kBN;
-    const bool has_next = tile + 1 < ntiles;
-    int bad = 0;
-    if (has_next) {
-      // index lookups for tile t+2 go out before the tile t+1 loads, so waiting
-      // for them (a step later) never waits for the bulk loads
-      load_tile_slots<D>(fill, rtt_row, t0 + 2 * kBN, kv_end, wave, lane);
-      dma_tile<D>(use, nxt, kbase, vbase, row_elems, a.pool_slots, wave, lane);
-      bad = invalid_mask<D>(use);
-    }
-    if (t0 <= wave_max_pos) compute_tile<D>(rs, cur, qop, t0, pos, wave_min_pos, c, lane);
-    wait_vmem_all();
-    if (bad) zero_invalid_rows<D>(bad, nxt, wave, lane);
+    // slots of tile+3 (wave 0; ring index J), then the K/V rows of tile+2: both
+    // are in flight while tiles tile and tile+1 are computed
+    if (wave == 0 && tile + 3 < ntiles) issue_slots(rtt_row, t0 + 3 * kBN, kv_end, slot0 + J * S::SLOT_BYTES, lane);
+    const bool kv2 = tile + 2 < ntiles;
+    if (kv2) issue_kv<D>(slot0 + J2 * S::SLOT_BYTES, kv0 + J2 * S::STAGE, kbase, vbase, row_elems, last_slot, wave, lane);
+    if (t0 <= wave_max_pos) compute_tile<D>(rs, kv0 + J * S::STAGE, qop, ko, vbo, t0, pos, wave_min_pos, c, lane);
+    // publish tile+1 and the slots of tile+3: all but tile+2's K/V loads have landed
+    if (kv2) wait_vmem<2 * S::NQ>(); else wait_vmem<0>();
+    if (tile + 1 < ntiles) zero_rows_past_end<D>(kv0 + J1 * S::STAGE, t0 + kBN, kv_end, wave, lane);
     __syncthreads();
   };
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    step(tile, stage0, stage1, sl_a, sl_b);
-    if (tile + 1 < ntiles) step(tile + 1, stage1, stage0, sl_b, sl_a);
+  for (int tile = 0; tile < ntiles; tile += 3) {
+    step(tile, std::integral_constant<int, 0>());
+    if (tile + 1 < ntiles) step(tile + 1, std::integral_constant<int, 1>());
+    if (tile + 2 < ntiles) step(tile + 2, std::integral_constant<int, 2>());
   }
+  wait_vmem<0>();
 
   // ---- epilogue: Oᵀ[d][row] -> out[token][h][d]
   float l = rs.lpart + __shfl_xor(rs.lpart, 32);

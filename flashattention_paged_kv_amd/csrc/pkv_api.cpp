@@ -160,7 +160,8 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
                     void* stream) {
   if (int rc = check_params(params, PKV_DECODE)) return rc;
   if (batch < 0) return fail(PKV_EINVAL, "batch=%d must be >= 0", batch);
-  if (pool_slots < 1) return fail(PKV_EINVAL, "pool_slots=%lld must be >= 1", (long long)pool_slots);
+  if (pool_slots < 1 || pool_slots > ((int64_t)1 << 31))
+    return fail(PKV_EINVAL, "pool_slots=%lld must be in [1, 2^31] (slots are int32)", (long long)pool_slots);
   if (rtt_stride < params->max_kv_len)
     return fail(PKV_EINVAL, "rtt_stride=%lld is smaller than max_kv_len=%d", (long long)rtt_stride, params->max_kv_len);
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.f)) return fail(PKV_EINVAL, "sm_scale must be finite and > 0");
@@ -231,7 +232,8 @@ int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void*
   if (int rc = check_params(params, PKV_EXTEND)) return rc;
   if (batch < 0) return fail(PKV_EINVAL, "batch=%d must be >= 0", batch);
   if (total_q < 0) return fail(PKV_EINVAL, "total_q=%lld must be >= 0", (long long)total_q);
-  if (pool_slots < 1) return fail(PKV_EINVAL, "pool_slots=%lld must be >= 1", (long long)pool_slots);
+  if (pool_slots < 1 || pool_slots > ((int64_t)1 << 31))
+    return fail(PKV_EINVAL, "pool_slots=%lld must be in [1, 2^31] (slots are int32)", (long long)pool_slots);
   if (rtt_stride < params->max_kv_len)
     return fail(PKV_EINVAL, "rtt_stride=%lld is smaller than max_kv_len=%d", (long long)rtt_stride, params->max_kv_len);
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.f)) return fail(PKV_EINVAL, "sm_scale must be finite and > 0");

@@ -13,7 +13,7 @@ namespace pkv {
 // ---------------------------------------------------------------- constants
 constexpr int kDecodeTile = 32;       // decode tokens per inner step (two 16-token MFMA blocks)
 constexpr int kDefaultSplitTarget = 4096;
-constexpr int kExtendRows = 128;      // (head, token) rows per extend work item (4 waves x 32)
+constexpr int kExtendRows = 256;      // (head, token) rows per extend work item (8 waves x 32)
 constexpr int kExtendTileN = 64;      // keys per extend inner step
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanLdsSortMax = 4096; // extend items sorted in LDS (32 KiB) up to this count

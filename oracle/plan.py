@@ -29,7 +29,7 @@ Decode rule (tile = 32 tokens):
   fixed: B · max(1, ceil(max_kv_len / kv_chunk)).
 
 Extend rule: rows of a work item are (head, token) pairs of one kv head,
-block_tokens = max(1, 128 // G) new tokens × G heads.  Request b contributes
+block_tokens = max(1, 256 // G) new tokens × G heads.  Request b contributes
 ceil(n_b / block_tokens) items (b, t) with kv_end = min(p_b + min((t+1)·block,
 n_b), L_b), p_b = L_b - n_b; items are ordered by kv_end descending (longest
 causal range first), ties by creation order.
@@ -41,7 +41,7 @@ from typing import Dict
 import numpy as np
 
 DECODE_TILE = 32
-EXTEND_BLOCK_M = 128  # rows ((head, token) pairs) per extend work item
+EXTEND_BLOCK_M = 256  # rows ((head, token) pairs) per extend work item
 DEFAULT_SPLIT_TARGET = 4096
 
 
