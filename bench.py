@@ -13,6 +13,19 @@ long-context decode and 8-bit decode workloads are reported in
 ``secondary`` with their own roofline figures.
 
 Prints ONE JSON line.  Inputs are resident in HBM before timing starts.
+
+Timing: ``ms_per_step`` spans the K timed steps (two events around them).
+Inside each step the stores of all layers are issued first and the attention
+calls of all layers follow back to back, bracketed by one event pair; the
+``roofline`` launch duration is that bracket divided by the layer count.  A
+decode attention call is the split-KV kernel followed by its merge kernel,
+so its duration is the sum of both kernels' times in a kernel trace.
+
+Two helper modes feed the ``traffic`` field of ``roofline``:
+``--copy-calibration`` runs a plain copy kernel of known size (1 GiB read,
+1 GiB written) for a counter run, and ``--ingest-counters`` turns the
+rocprofv3 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` CSV files of a workload
+and of that copy into ``profiles/traffic_<workload>.json``.
 """
 from __future__ import annotations
 
@@ -61,6 +74,80 @@ def traffic_from_counters(workload: str):
     return t.get("traffic_bytes_per_launch")
 
 
+# Kernels that make up one attention call of each workload, as rocprofv3 names them.
+CALL_KERNELS = {
+    "decode_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
+    "long_decode_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
+    "decode_fp8": ("decode_fp8_kernel", "decode_merge_kernel"),
+    "extend_bf16": ("extend_bf16_kernel",),
+}
+COPY_BYTES = 1 << 30
+
+
+def _counter_per_dispatch(path: str, counter: str):
+    """{kernel substring match -> (dispatches, average value)} from a rocprofv3 counter CSV."""
+    import collections
+    import csv
+    per = collections.defaultdict(float)
+    names = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    return per, names
+
+
+def _avg_for(per, names, needle):
+    vals = [v for d, v in per.items() if needle in names[d]]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {needle!r} in the counter file")
+    return len(vals), sum(vals) / len(vals)
+
+
+def ingest_counters(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, commands):
+    """Scale the kernels' FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the
+    same counters read for the plain 1 GiB copy, and store bytes per attention call."""
+    cf, cn = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE")
+    cw, cwn = _counter_per_dispatch(copy_write_csv, "WRITE_SIZE")
+    # the copy is the only kernel with a 1 GiB footprint: take the largest dispatches
+    copy_fetch = max(cf.values()) * 1024.0
+    copy_write = max(cw.values()) * 1024.0
+    fetch_factor, write_factor = copy_fetch / COPY_BYTES, copy_write / COPY_BYTES
+    kf, kfn = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
+    kw, kwn = _counter_per_dispatch(write_csv, "WRITE_SIZE")
+    kernels = {}
+    total = 0.0
+    for k in CALL_KERNELS[workload]:
+        nf, f = _avg_for(kf, kfn, k)
+        nw, w = _avg_for(kw, kwn, k)
+        fb, wb = f * 1024.0 / fetch_factor, w * 1024.0 / write_factor
+        kernels[k] = {"dispatches": [nf, nw], "fetch_kib": round(f, 1), "write_kib": round(w, 1),
+                      "fetch_bytes": round(fb), "write_bytes": round(wb)}
+        total += fb + wb
+    out = {"workload": workload, "source_sha": source_hash(workload), "kernels": kernels,
+           "copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                                "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)},
+           "traffic_bytes_per_launch": round(total), "commands": commands}
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+def copy_calibration():
+    """A plain streaming kernel of known size: 1 GiB read once, 1 GiB written once."""
+    import torch
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "kernel": "torch.neg (bf16 elementwise)"}), flush=True)
+
+
 # ---------------------------------------------------------------- workloads
 class DecodeRunner:
     def __init__(self, name, layers, torch, pkv, workloads):
@@ -90,15 +177,14 @@ class DecodeRunner:
         plan = pkv.plan_metadata(self.params, pkv.PKV_DECODE, db.seq_lens, workspace=self.ws)
         for l in range(self.layers):
             pkv.kv_store(self.params, db.k_pools[l], db.v_pools[l], db.k_new[l], db.v_new[l], db.new_slots)
-            if events is not None:
-                events.append(self.torch.cuda.Event(enable_timing=True))
-                events[-1].record()
+        if events is not None:
+            events[0].record()
+        for l in range(self.layers):
             pkv.attn_decode(self.params, db.q, db.k_pools[l], db.v_pools[l], db.req_to_token, db.seq_lens, plan,
                             scratch=self.scratch, out=self.out[l], lse=self.lse,
                             sfq=db.sfq, sfk=db.sfk, sfv=db.sfv)
-            if events is not None:
-                events.append(self.torch.cuda.Event(enable_timing=True))
-                events[-1].record()
+        if events is not None:
+            events[1].record()
 
     def describe(self):
         s = self.spec
@@ -112,7 +198,7 @@ class DecodeRunner:
         achieved = self.kv_bytes_per_layer / avg_launch_s / 1e9
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_from_counters(workload),
-                "kernel": "decode_fp8_kernel + merge" if self.fp8 else "decode_bf16_kernel + decode_merge_kernel",
+                "kernel": " + ".join(CALL_KERNELS[workload]),
                 "algorithmic_bytes_per_launch": self.kv_bytes_per_layer,
                 "avg_launch_us": round(avg_launch_s * 1e6, 2)}
 
@@ -132,7 +218,8 @@ class DecodeRunner:
             vp = db.v_pools[0].float().cpu().numpy()
         done_bytes, n = 0, 0
         t0 = time.perf_counter()
-        for b in range(spec.batch):
+        while time.perf_counter() - t0 < budget_s:  # whole passes over the batch, then a partial one
+            b = n % spec.batch
             rtt = lay.req_to_token[b:b + 1]
             L = lay.seq_lens[b:b + 1]
             if self.fp8:
@@ -142,11 +229,10 @@ class DecodeRunner:
                 oracle.paged_attention(q[b:b + 1], kp, vp, rtt, L, [0, 1])
             done_bytes += int(L[0]) * spec.num_kv_heads * spec.head_dim * 2 * (1 if self.fp8 else 2)
             n += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
         dt = time.perf_counter() - t0
         return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "seconds": round(dt, 2),
-                "sample": f"layer 0, requests 0..{n - 1} of {spec.batch} ({spec.name}), all {spec.num_q_heads} heads"}
+                "sample": f"layer 0 of {spec.name}: {n} request-attentions ({n / spec.batch:.1f} passes over "
+                          f"the {spec.batch}-request batch), all {spec.num_q_heads} heads, fp64"}
 
 
 class ExtendRunner:
@@ -177,14 +263,13 @@ class ExtendRunner:
                                  workspace=self.ws)
         for l in range(self.layers):
             pkv.kv_store(self.params, db.k_pools[l], db.v_pools[l], db.k_new[l], db.v_new[l], db.new_slots)
-            if events is not None:
-                events.append(self.torch.cuda.Event(enable_timing=True))
-                events[-1].record()
+        if events is not None:
+            events[0].record()
+        for l in range(self.layers):
             pkv.attn_extend(self.params, db.q, db.k_pools[l], db.v_pools[l], db.req_to_token, db.seq_lens,
                             db.cu_seqlens_q, plan, out=self.out[l], lse=self.lse)
-            if events is not None:
-                events.append(self.torch.cuda.Event(enable_timing=True))
-                events[-1].record()
+        if events is not None:
+            events[1].record()
 
     def describe(self):
         s = self.spec
@@ -212,17 +297,18 @@ def measure(name, steps, warmup, layers, torch, pkv, workloads):
     for _ in range(warmup):
         runner.step()
     torch.cuda.synchronize()
-    events = []
+    # one event pair per step around the attention block (all layers back to back):
+    # every event record adds a few microseconds of queue gap, so none sit between launches
+    blocks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for _ in range(steps):
-        runner.step(events)
+    for i in range(steps):
+        runner.step(blocks[i])
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
-    launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(0, len(events), 2)]
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    avg_launch_s = sum(a.elapsed_time(b) for a, b in blocks) / (steps * runner.layers) / 1e3
     scale = 1e9 if UNITS[name] == "GB/s" else 1e12
     value = runner.work_per_step / (ms / 1e3) / scale
     return runner, ms, value, runner.roofline(avg_launch_s, name)
@@ -239,11 +325,22 @@ def main():
                     help="comma list of workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true", help="run only the 1 GiB copy (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV files (host only)")
+    ap.add_argument("--commands", default="", help="with --ingest-counters: the profiler commands, ' ;; '-separated")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(args.workload, *args.ingest_counters,
+                        commands=[c.strip() for c in args.commands.split(";;") if c.strip()])
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the path shards by request or kv head with no exchange)"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     import flashattention_paged_kv_amd as pkv

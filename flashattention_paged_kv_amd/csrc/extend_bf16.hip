@@ -13,7 +13,7 @@
 // workgroup fills a CU (two waves per SIMD).
 //
 // Data movement is asynchronous and register-free: global -> LDS loads
-// (gfx950 global_load_lds_*) fill a ring of three K/V stages and four slot
+// (gfx950 global_load_lds_*) fill a ring of three K/V stages and three slot
 // stages.  While tile t is computed, the K/V rows of tile t+2 and the
 // req_to_token entries of tile t+3 are in flight; the slots of a tile are
 // read from LDS one step before its K/V rows are requested.  The tile loop is
