@@ -35,31 +35,37 @@ struct KVTile {
   u32x4 v[8];      // the lane's 8 V rows, elements d = 8*(lane%16) .. +8
 };
 
-// Lane l's token slot for positions t0 + (l & 31) of the tile (-1 past the range).
-__device__ __forceinline__ int tile_slot(const int32_t* __restrict__ rtt_row, int t0, int kv_end,
-                                         int64_t pool_slots, int lane) {
-  const int tok = t0 + (lane & 31);
-  return tok < kv_end ? clamp_slot(rtt_row[tok], pool_slots) : -1;
+// Lane l's token slot for position t0 + (l & 31) of the tile.  Positions past
+// the item's range are clamped to its last token, so every load below is
+// unconditional (straight-line code keeps the compiler's load counting exact)
+// and re-reads a row already fetched; their scores are masked to -inf.
+__device__ __forceinline__ uint32_t tile_slot(const int32_t* __restrict__ rtt_row, int t0, int kv_end,
+                                              uint32_t last, int lane) {
+  const int tok = min(t0 + (lane & 31), kv_end - 1);
+  return clamp_slot_u32(rtt_row[tok], last);
 }
 
 template <int D>
-__device__ __forceinline__ void load_tile(KVTile<D>& t, int slot, const uint16_t* __restrict__ kbase,
-                                          const uint16_t* __restrict__ vbase, int64_t row_elems, int lane) {
+__device__ __forceinline__ void load_tile(KVTile<D>& t, uint32_t slot, const uint16_t* __restrict__ kbase,
+                                          const uint16_t* __restrict__ vbase, uint32_t row_elems, int lane) {
   constexpr int KB = D / 32;
   const int l16 = lane & 15, j = lane >> 4;
-  const int sk0 = __shfl(slot, l16), sk1 = __shfl(slot, 16 + l16);
-  const u32x4 z = {0u, 0u, 0u, 0u};
+  const uint32_t sk0 = __shfl(slot, l16), sk1 = __shfl(slot, 16 + l16);
+  const uint16_t* k0 = kbase + row_offset(sk0, row_elems) + 8 * j;
+  const uint16_t* k1 = kbase + row_offset(sk1, row_elems) + 8 * j;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    t.k[0][kb] = sk0 >= 0 ? ldg16(kbase + (int64_t)sk0 * row_elems + 32 * kb + 8 * j) : z;
-    t.k[1][kb] = sk1 >= 0 ? ldg16(kbase + (int64_t)sk1 * row_elems + 32 * kb + 8 * j) : z;
+    t.k[0][kb] = ldg16(k0 + 32 * kb);
+    t.k[1][kb] = ldg16(k1 + 32 * kb);
   }
-  const bool d_ok = (D == 128) || (l16 < D / 8);
+  // d = 64: lanes 8..15 re-read columns of their own row; they only feed
+  // output rows d >= 64, which are never stored
+  const int dcol = 8 * (l16 & (D / 8 - 1));
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int tau = r < 4 ? 4 * j + r : 16 + 4 * j + (r - 4);
-    const int sv = __shfl(slot, tau);
-    t.v[r] = (sv >= 0 && d_ok) ? ldg16(vbase + (int64_t)sv * row_elems + 8 * l16) : z;
+    const uint32_t sv = __shfl(slot, tau);
+    t.v[r] = ldg16(vbase + row_offset(sv, row_elems) + dcol);
   }
 }
 
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
   const int h = g * a.group + hl;
   const int row = a.rpi ? a.rpi[b] : b;
   const int32_t* __restrict__ rtt_row = a.rtt + (int64_t)row * a.rtt_stride;
-  const int64_t row_elems = (int64_t)a.hkv * D;
+  const uint32_t row_elems = (uint32_t)a.hkv * D;
   const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * D;
   const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * D;
 
@@ -152,16 +158,28 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int e = 0; e < 8; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   if (kv_begin < kv_end) {
-    KVTile<D> cur, nxt;
-    int slot_n = tile_slot(rtt_row, kv_begin, kv_end, a.pool_slots, lane);
-    load_tile<D>(cur, slot_n, kbase, vbase, row_elems, lane);
-    slot_n = tile_slot(rtt_row, kv_begin + kDecodeTile, kv_end, a.pool_slots, lane);
-    for (int t0 = kv_begin; t0 < kv_end; t0 += kDecodeTile) {
-      const int slot_nn = tile_slot(rtt_row, t0 + 2 * kDecodeTile, kv_end, a.pool_slots, lane);
-      load_tile<D>(nxt, slot_n, kbase, vbase, row_elems, lane);
-      compute_tile<D>(cur, qop, t0, kv_end, a.scale_log2, m, lpart, acc, lane);
-      cur = nxt;
-      slot_n = slot_nn;
+    // Software pipeline over 32-token tiles, two register buffers used in
+    // turn: while tile i is computed, the K/V rows of tile i+1 are in flight
+    // and the slots of tile i+2 were requested before them, so waiting for a
+    // slot never waits for the K/V rows issued after it.
+    const uint32_t last = (uint32_t)(a.pool_slots - 1);
+    KVTile<D> ta, tb;
+    uint32_t s_odd, s_even = tile_slot(rtt_row, kv_begin, kv_end, last, lane);
+    load_tile<D>(ta, s_even, kbase, vbase, row_elems, lane);
+    s_odd = tile_slot(rtt_row, kv_begin + kDecodeTile, kv_end, last, lane);
+    for (int t0 = kv_begin;;) {
+      s_even = tile_slot(rtt_row, t0 + 2 * kDecodeTile, kv_end, last, lane);
+      load_tile<D>(tb, s_odd, kbase, vbase, row_elems, lane);
+      __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
+      compute_tile<D>(ta, qop, t0, kv_end, a.scale_log2, m, lpart, acc, lane);
+      t0 += kDecodeTile;
+      if (t0 >= kv_end) break;
+      s_odd = tile_slot(rtt_row, t0 + 2 * kDecodeTile, kv_end, last, lane);
+      load_tile<D>(ta, s_even, kbase, vbase, row_elems, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile<D>(tb, qop, t0, kv_end, a.scale_log2, m, lpart, acc, lane);
+      t0 += kDecodeTile;
+      if (t0 >= kv_end) break;
     }
   }
 
@@ -210,7 +228,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacit
   if (capacity <= 0 || batch <= 0) return hipSuccess;
   // up to 8 waves per workgroup: the kv heads of one split run side by side
   const int units = a.hkv * a.head_groups;
-  const int wpb = units >= 8 ? 8 : (units >= 4 ? 4 : (units >= 2 ? 2 : 1));
+  const int wpb = decode_waves_per_block(units);
   dim3 grid((unsigned)capacity, (unsigned)ceil_div(units, wpb));
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * wpb), 0, s, a); };
   if (head_dim == 128) {
@@ -221,6 +239,29 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacit
     else if (wpb == 2) go(decode_bf16_kernel<64, 2>); else go(decode_bf16_kernel<64, 1>);
   }
   return hipGetLastError();
+}
+
+hipError_t resident_items_of(const void* kernel, int wpb, int units, int64_t* items) {
+  int dev = 0, cus = 0, blocks = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, 64 * wpb, 0);
+  if (e != hipSuccess) return e;
+  const int64_t per_item = ceil_div(units, wpb);  // workgroups of one item
+  *items = (int64_t)cus * blocks / per_item;
+  return hipSuccess;
+}
+
+hipError_t decode_bf16_resident_items(int head_dim, int units, int64_t* items) {
+  const int wpb = decode_waves_per_block(units);
+  const void* k = nullptr;
+  if (head_dim == 128)
+    k = wpb == 8 ? (const void*)decode_bf16_kernel<128, 8> : wpb == 4 ? (const void*)decode_bf16_kernel<128, 4>
+      : wpb == 2 ? (const void*)decode_bf16_kernel<128, 2> : (const void*)decode_bf16_kernel<128, 1>;
+  else
+    k = wpb == 8 ? (const void*)decode_bf16_kernel<64, 8> : wpb == 4 ? (const void*)decode_bf16_kernel<64, 4>
+      : wpb == 2 ? (const void*)decode_bf16_kernel<64, 2> : (const void*)decode_bf16_kernel<64, 1>;
+  return resident_items_of(k, wpb, units, items);
 }
 
 }  // namespace pkv

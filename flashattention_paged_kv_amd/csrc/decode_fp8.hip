@@ -235,12 +235,19 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity
   (void)head_dim;  // 128 only (validated by the host API)
   if (capacity <= 0 || batch <= 0) return hipSuccess;
   const int units = a.hkv * a.head_groups;
-  const int wpb = units >= 8 ? 8 : (units >= 4 ? 4 : (units >= 2 ? 2 : 1));
+  const int wpb = decode_waves_per_block(units);
   dim3 grid((unsigned)capacity, (unsigned)ceil_div(units, wpb));
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * wpb), 0, s, a); };
   if (wpb == 8) go(decode_fp8_kernel<8>); else if (wpb == 4) go(decode_fp8_kernel<4>);
   else if (wpb == 2) go(decode_fp8_kernel<2>); else go(decode_fp8_kernel<1>);
   return hipGetLastError();
+}
+
+hipError_t decode_fp8_resident_items(int units, int64_t* items) {
+  const int wpb = decode_waves_per_block(units);
+  const void* k = wpb == 8 ? (const void*)decode_fp8_kernel<8> : wpb == 4 ? (const void*)decode_fp8_kernel<4>
+                : wpb == 2 ? (const void*)decode_fp8_kernel<2> : (const void*)decode_fp8_kernel<1>;
+  return resident_items_of(k, wpb, units, items);
 }
 
 }  // namespace pkv

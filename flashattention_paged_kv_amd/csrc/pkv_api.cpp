@@ -7,7 +7,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
+#include <tuple>
 
 #include "pkv_internal.h"
 
@@ -70,6 +73,43 @@ int check_params(const pkv_params* p, int mode) {
 
 int64_t elem_bytes(const pkv_params* p) { return p->kv_dtype == PKV_FP8_E4M3 ? 1 : 2; }
 
+// Decode items the current device holds at once for these params (cached per
+// device and kernel variant).  Without a device (host-only sizing) the
+// library assumes 256 CUs x 16 resident waves.
+int64_t resident_items(const pkv_params& p) {
+  const int units = (int)pkv::decode_units(p);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    const int wpb = pkv::decode_waves_per_block(units);
+    const int64_t blocks = pkv::kFallbackResidentWaves / wpb;
+    const int64_t r = blocks / pkv::ceil_div(units, wpb);
+    return r > 1 ? r : 1;
+  }
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int>, int64_t> cache;
+  const auto key = std::make_tuple(dev, (int)p.kv_dtype, p.head_dim, units);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int64_t items = 0;
+  hipError_t e = p.kv_dtype == PKV_FP8_E4M3 ? pkv::decode_fp8_resident_items(units, &items)
+                                             : pkv::decode_bf16_resident_items(p.head_dim, units, &items);
+  if (e != hipSuccess || items < 1) {
+    (void)hipGetLastError();
+    items = 1;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  cache[key] = items;
+  return items;
+}
+
+int64_t target_items(const pkv_params& p, int mode) {
+  return mode == PKV_DECODE ? pkv::decode_target_items(p, p.split_target > 0 ? 1 : resident_items(p)) : 0;
+}
+
 int check_launch(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -89,9 +129,10 @@ int pkv_workspace_size(const pkv_params* params, int32_t mode, int32_t max_batch
   if (max_batch < 0) return fail(PKV_EINVAL, "max_batch=%d must be >= 0", max_batch);
   if (max_total_q < 0) return fail(PKV_EINVAL, "max_total_q=%lld must be >= 0", (long long)max_total_q);
   if (!workspace_bytes || !scratch_bytes) return fail(PKV_EINVAL, "output pointers must not be NULL");
-  const pkv::WsLayout w = pkv::ws_layout(*params, mode, max_batch, max_total_q);
+  const int64_t tgt = target_items(*params, mode);
+  const pkv::WsLayout w = pkv::ws_layout(*params, mode, max_batch, max_total_q, tgt);
   *workspace_bytes = (size_t)(w.total_ints * 4);
-  *scratch_bytes = mode == PKV_DECODE ? (size_t)pkv::decode_scratch(*params, max_batch).total_bytes : 0;
+  *scratch_bytes = mode == PKV_DECODE ? (size_t)pkv::decode_scratch(*params, max_batch, tgt).total_bytes : 0;
   return ok();
 }
 
@@ -106,12 +147,12 @@ int pkv_plan_metadata(const pkv_params* params, int32_t mode, int32_t batch, int
   if (mode == PKV_EXTEND && batch > 0 && !cu_seqlens_q) return fail(PKV_EINVAL, "cu_seqlens_q is NULL for an extend plan");
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
   const int64_t tq = mode == PKV_EXTEND ? total_q : 0;
-  const pkv::WsLayout w = pkv::ws_layout(*params, mode, batch, tq);
+  const int64_t tgt = target_items(*params, mode);
+  const pkv::WsLayout w = pkv::ws_layout(*params, mode, batch, tq, tgt);
   if ((int64_t)workspace_bytes < w.total_ints * 4)
     return fail(PKV_EWORKSPACE, "workspace_bytes=%zu is smaller than the %lld bytes required", workspace_bytes,
                 (long long)(w.total_ints * 4));
   if (w.capacity > INT32_MAX) return fail(PKV_EUNSUPPORTED, "work-item capacity %lld exceeds int32", (long long)w.capacity);
-  const int group = params->num_q_heads / params->num_kv_heads;
   pkv::PlanArgs a{};
   a.seq_lens = seq_lens;
   a.cu_seqlens_q = cu_seqlens_q;
@@ -126,12 +167,8 @@ int pkv_plan_metadata(const pkv_params* params, int32_t mode, int32_t batch, int
   a.mode = mode;
   a.max_kv_len = params->max_kv_len;
   a.kv_chunk = params->kv_chunk;
-  {
-    const int64_t units = (int64_t)params->num_kv_heads * pkv::ceil_div(group, 16);
-    const int64_t tgt = params->split_target > 0 ? params->split_target : pkv::kDefaultSplitTarget;
-    int64_t ts = pkv::ceil_div(tgt, units);
-    a.target_splits = (int32_t)(ts < 1 ? 1 : ts);
-  }
+  if (tgt > INT32_MAX) return fail(PKV_EUNSUPPORTED, "split target %lld exceeds int32", (long long)tgt);
+  a.target_items = (int32_t)tgt;
   a.block_tokens = pkv::extend_block_tokens(*params);
   return check_launch(pkv::launch_plan(a, static_cast<hipStream_t>(stream)), "plan_metadata launch");
 }
@@ -179,11 +216,12 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
     return fail(PKV_EINVAL, "a required pointer (out, q, pools, req_to_token, seq_lens, workspace) is NULL");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PKV_EINVAL, "out, q and the pools must be 16-byte aligned");
-  const pkv::WsLayout w = pkv::ws_layout(*params, PKV_DECODE, batch, 0);
+  const int64_t tgt = target_items(*params, PKV_DECODE);
+  const pkv::WsLayout w = pkv::ws_layout(*params, PKV_DECODE, batch, 0, tgt);
   if ((int64_t)workspace_bytes < w.total_ints * 4)
     return fail(PKV_EWORKSPACE, "workspace_bytes=%zu is smaller than the %lld bytes required", workspace_bytes,
                 (long long)(w.total_ints * 4));
-  const pkv::DecodeScratch sc = pkv::decode_scratch(*params, batch);
+  const pkv::DecodeScratch sc = pkv::decode_scratch(*params, batch, tgt);
   if (!scratch || (int64_t)scratch_bytes < sc.total_bytes)
     return fail(PKV_EWORKSPACE, "scratch_bytes=%zu is smaller than the %lld bytes required", scratch ? scratch_bytes : 0,
                 (long long)sc.total_bytes);
@@ -242,7 +280,7 @@ int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void*
     return fail(PKV_EINVAL, "a required pointer (out, q, pools, req_to_token, seq_lens, cu_seqlens_q, workspace) is NULL");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PKV_EINVAL, "out, q and the pools must be 16-byte aligned");
-  const pkv::WsLayout w = pkv::ws_layout(*params, PKV_EXTEND, batch, total_q);
+  const pkv::WsLayout w = pkv::ws_layout(*params, PKV_EXTEND, batch, total_q, 0);
   if ((int64_t)workspace_bytes < w.total_ints * 4)
     return fail(PKV_EWORKSPACE, "workspace_bytes=%zu is smaller than the %lld bytes required", workspace_bytes,
                 (long long)(w.total_ints * 4));

@@ -12,7 +12,8 @@ namespace pkv {
 
 // ---------------------------------------------------------------- constants
 constexpr int kDecodeTile = 32;       // decode tokens per inner step (two 16-token MFMA blocks)
-constexpr int kDefaultSplitTarget = 4096;
+// Resident decode waves assumed when no device can be queried (256 CUs x 16).
+constexpr int kFallbackResidentWaves = 4096;
 constexpr int kExtendRows = 256;      // (head, token) rows per extend work item (8 waves x 32)
 constexpr int kExtendTileN = 64;      // keys per extend inner step
 constexpr int kPlanThreads = 1024;
@@ -25,6 +26,7 @@ enum : int {
   WS_NUM_ITEMS = 2,
   WS_CAPACITY = 3,
   WS_CHUNK = 4,  // decode: chunk tiles; extend: block tokens
+  WS_TARGET = 5, // decode: the item count the chunk was sized for
   WS_HEADER_INTS = 16
 };
 
@@ -52,18 +54,23 @@ inline int64_t decode_units(const pkv_params& p) {
   return (int64_t)p.num_kv_heads * ceil_div(p.num_q_heads / p.num_kv_heads, 16);
 }
 
-inline int64_t decode_capacity(const pkv_params& p, int64_t batch) {
-  const int64_t group = p.num_q_heads / p.num_kv_heads;
-  const int64_t units = (int64_t)p.num_kv_heads * ceil_div(group, 16);
-  const int64_t tgt = p.split_target > 0 ? p.split_target : kDefaultSplitTarget;
+// Split items the automatic chunk is sized for: by default the number of
+// items whose waves the device holds at once (`resident_items`, from the
+// decode kernel's occupancy), so a launch runs in one pass with no tail of
+// late waves; a positive split_target asks for ceil(split_target / units).
+inline int64_t decode_target_items(const pkv_params& p, int64_t resident_items) {
+  const int64_t t = p.split_target > 0 ? ceil_div(p.split_target, decode_units(p)) : resident_items;
+  return t > 1 ? t : 1;
+}
+
+inline int64_t decode_capacity(const pkv_params& p, int64_t batch, int64_t target_items) {
   const int64_t max_tiles = ceil_div(p.max_kv_len, kDecodeTile) > 0 ? ceil_div(p.max_kv_len, kDecodeTile) : 1;
   if (p.kv_chunk > 0) {
     int64_t per = ceil_div(p.max_kv_len, p.kv_chunk);
     return batch * (per > 0 ? per : 1);
   }
-  int64_t target_splits = ceil_div(tgt, units);
-  if (target_splits < 1) target_splits = 1;
-  int64_t a = target_splits + batch, b = batch * max_tiles;
+  // the chunk search never gives more than max(target, batch) items
+  const int64_t a = target_items > batch ? target_items : batch, b = batch * max_tiles;
   return a < b ? a : b;
 }
 
@@ -77,11 +84,11 @@ inline int64_t extend_capacity(const pkv_params& p, int64_t batch, int64_t total
   return ceil_div(total_q, extend_block_tokens(p)) + batch;
 }
 
-inline WsLayout ws_layout(const pkv_params& p, int mode, int64_t batch, int64_t total_q) {
+inline WsLayout ws_layout(const pkv_params& p, int mode, int64_t batch, int64_t total_q, int64_t target_items) {
   WsLayout w;
   w.req_off = WS_HEADER_INTS;
   w.items_off = align_up(w.req_off + batch + 1, 4);
-  w.capacity = mode == PKV_DECODE ? decode_capacity(p, batch) : extend_capacity(p, batch, total_q);
+  w.capacity = mode == PKV_DECODE ? decode_capacity(p, batch, target_items) : extend_capacity(p, batch, total_q);
   w.tmp_off = w.items_off + 4 * w.capacity;
   w.keys_off = align_up(w.tmp_off + 4 * w.capacity, 2);
   w.total_ints = w.keys_off + 2 * next_pow2(w.capacity > 0 ? w.capacity : 1);
@@ -95,9 +102,9 @@ struct DecodeScratch {
   int64_t total_bytes = 0;
 };
 
-inline DecodeScratch decode_scratch(const pkv_params& p, int64_t batch) {
+inline DecodeScratch decode_scratch(const pkv_params& p, int64_t batch, int64_t target_items) {
   DecodeScratch s;
-  const int64_t cap = decode_capacity(p, batch);
+  const int64_t cap = decode_capacity(p, batch, target_items);
   s.part_o_bytes = align_up(cap * p.num_q_heads * p.head_dim * (int64_t)sizeof(float), 256);
   s.part_lse_off = s.part_o_bytes;
   s.total_bytes = s.part_o_bytes + align_up(cap * p.num_q_heads * (int64_t)sizeof(float), 256);
@@ -116,7 +123,7 @@ struct PlanArgs {
   int32_t mode;
   int32_t max_kv_len;
   int32_t kv_chunk;
-  int32_t target_splits;
+  int32_t target_items;
   int32_t block_tokens;
 };
 
@@ -174,6 +181,13 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacit
 hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
                              hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int32_t batch, hipStream_t s);
+// Work items (all their waves) of a decode launch that the current device
+// holds at once, from the kernel's occupancy and the CU count.
+hipError_t decode_bf16_resident_items(int head_dim, int units, int64_t* items);
+hipError_t decode_fp8_resident_items(int units, int64_t* items);
+hipError_t resident_items_of(const void* kernel, int wpb, int units, int64_t* items);
+// Waves per workgroup the decode launchers use for `units` waves per item.
+inline int decode_waves_per_block(int units) { return units >= 8 ? 8 : (units >= 4 ? 4 : (units >= 2 ? 2 : 1)); }
 hipError_t launch_extend_bf16(const ExtendArgs& a, int head_dim, int64_t capacity, hipStream_t s);
 
 }  // namespace pkv

@@ -4,9 +4,17 @@
 // as the sglang get_scheduler_metadata analysis describes (intro, code §1-3).
 //
 // One workgroup of 1024 threads: block reductions / scans over the requests,
-// then an item table written in parallel and ordered longest-first (decode:
-// by split length; extend: by causal KV range) with a bitonic sort, in LDS up
-// to kPlanLdsSortMax items and in the workspace's key area beyond that.
+// then an item table written in parallel.
+//
+// Decode: the automatic chunk is the smallest number of 32-token tiles for
+// which the batch splits into at most target_items items (the items whose
+// waves the device holds at once), found by bisection over the chunk size;
+// the launch then runs in one pass.  Items stay in request order unless they
+// exceed that count (many short requests, or a fixed kv_chunk), in which case
+// they are ordered longest first so the short ones fill the tail.
+// Extend: items are ordered by causal KV range, longest first.
+// Ordering is a bitonic sort on (length, index) keys, in LDS up to
+// kPlanLdsSortMax items and in the workspace's key area beyond that.
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -46,6 +54,26 @@ __device__ int64_t block_exclusive_scan(int64_t v, int64_t* sh /*[16]*/, int64_t
   *total = sh[16];
   __syncthreads();
   return ex;
+}
+
+__device__ int64_t block_max(int64_t v, int64_t* sh /*[17]*/) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    int64_t u = __shfl_xor(v, off, 64);
+    v = u > v ? u : v;
+  }
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t m = sh[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = sh[w] > m ? sh[w] : m;
+    sh[16] = m;
+  }
+  __syncthreads();
+  const int64_t r = sh[16];
+  __syncthreads();
+  return r;
 }
 
 __device__ __forceinline__ int clamp_len(int L, int max_kv_len) {
@@ -98,18 +126,47 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   int64_t carry = 0;
 
   if (a.mode == PKV_DECODE) {
-    // 1. total tiles
-    int64_t my_tiles = 0;
-    for (int b = threadIdx.x; b < B; b += blockDim.x)
-      my_tiles += (clamp_len(a.seq_lens[b], a.max_kv_len) + kDecodeTile - 1) / kDecodeTile;
+    // 1. total and largest tile counts
+    int64_t my_tiles = 0, my_max = 0;
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+      const int64_t t = (clamp_len(a.seq_lens[b], a.max_kv_len) + kDecodeTile - 1) / kDecodeTile;
+      my_tiles += t;
+      my_max = t > my_max ? t : my_max;
+    }
     int64_t total_tiles;
     (void)block_exclusive_scan(my_tiles, sh, &total_tiles);
+    const int64_t max_tiles = block_max(my_max, sh);
+    // items the batch splits into for a chunk of c tiles (a request has >= 1)
+    auto count_items = [&](int64_t c) {
+      int64_t mine = 0;
+      for (int b = threadIdx.x; b < B; b += blockDim.x) {
+        const int64_t t = (clamp_len(a.seq_lens[b], a.max_kv_len) + kDecodeTile - 1) / kDecodeTile;
+        const int64_t n = (t + c - 1) / c;
+        mine += n < 1 ? 1 : n;
+      }
+      int64_t tot;
+      (void)block_exclusive_scan(mine, sh, &tot);
+      return tot;
+    };
     int64_t chunk;
     if (a.kv_chunk > 0) {
       chunk = a.kv_chunk / kDecodeTile;
     } else {
-      chunk = (total_tiles + a.target_splits - 1) / a.target_splits;
-      if (chunk < 1) chunk = 1;
+      // smallest chunk with count_items(chunk) <= target (count is non-increasing
+      // in the chunk; at max_tiles every request is one item)
+      const int64_t T = a.target_items;
+      int64_t hi = max_tiles > 0 ? max_tiles : 1;
+      int64_t lo = (total_tiles + T - 1) / T;
+      lo = lo < 1 ? 1 : (lo > hi ? hi : lo);
+      if (count_items(hi) > T) {
+        chunk = hi;
+      } else {
+        while (lo < hi) {  // block-uniform: every bound comes from a block total
+          const int64_t mid = (lo + hi) >> 1;
+          if (count_items(mid) <= T) hi = mid; else lo = mid + 1;
+        }
+        chunk = lo;
+      }
     }
     // 2. splits per request, exclusive scan -> req[]
     for (int base = 0; base < B; base += blockDim.x) {
@@ -130,9 +187,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     __threadfence_block();
     __syncthreads();
     // 3. items (b, kv_begin, kv_end, partial index), created request-major;
-    //    the partial index of split s of request b is req[b] + s
-    int4* tmp = reinterpret_cast<int4*>(ws + a.tmp_off);
-    const int n2 = sort_size(num);
+    //    the partial index of split s of request b is req[b] + s.  Sorted
+    //    (through tmp) only when they overflow the target.
+    const bool sorted = num > a.target_items;
+    int4* tmp = reinterpret_cast<int4*>(ws + (sorted ? a.tmp_off : a.items_off));
+    const int n2 = sorted ? sort_size(num) : (int)num;
     const bool in_lds = n2 <= kPlanLdsSortMax;
     uint64_t* keys_g = reinterpret_cast<uint64_t*>(ws + a.keys_off);
     for (int64_t i = threadIdx.x; i < n2; i += blockDim.x) {
@@ -150,15 +209,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         tmp[i] = make_int4(b, kb, ke, n > 1 ? (int)i : -1);
         key = ((uint64_t)(uint32_t)(0x7fffffff - (ke - kb)) << 32) | (uint64_t)i;  // longest split first
       }
+      if (!sorted) continue;
       if (in_lds) keys_lds[i] = key; else keys_g[i] = key;
     }
-    __threadfence_block();
-    __syncthreads();
-    if (in_lds) bitonic_sort_u64(keys_lds, n2);
-    else bitonic_sort_u64(keys_g, n2);
-    for (int64_t j = threadIdx.x; j < num; j += blockDim.x) {
-      uint64_t key = in_lds ? keys_lds[j] : keys_g[j];
-      items[j] = tmp[(uint32_t)(key & 0xffffffffu)];
+    if (sorted) {
+      __threadfence_block();
+      __syncthreads();
+      if (in_lds) bitonic_sort_u64(keys_lds, n2);
+      else bitonic_sort_u64(keys_g, n2);
+      for (int64_t j = threadIdx.x; j < num; j += blockDim.x) {
+        uint64_t key = in_lds ? keys_lds[j] : keys_g[j];
+        items[j] = tmp[(uint32_t)(key & 0xffffffffu)];
+      }
     }
     if (threadIdx.x == 0) {
       ws[WS_MODE] = PKV_DECODE;
@@ -166,6 +228,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       ws[WS_NUM_ITEMS] = (int32_t)num;
       ws[WS_CAPACITY] = (int32_t)a.capacity;
       ws[WS_CHUNK] = (int32_t)chunk;
+      ws[WS_TARGET] = a.target_items;
     }
     return;
   }

@@ -95,13 +95,17 @@ typedef struct pkv_params {
   int32_t k_block;      /* 8-bit: key positions per sfK block, a multiple of 16; else 0 */
   int32_t max_kv_len;   /* upper bound of seq_lens (>= 1, <= rtt_stride of the run calls) */
   int32_t kv_chunk;     /* DECODE split size in tokens: 0 = automatic, else a multiple of 32 */
-  int32_t split_target; /* DECODE automatic mode: target work items per call (0 = 4096) */
+  int32_t split_target; /* DECODE automatic mode: waves per call to size splits for; 0 = as many
+                           as the current device holds at once (from the kernel's occupancy;
+                           256 CUs x 16 when no device is present) */
 } pkv_params;
 
 /* Sizes of the plan workspace (written by pkv_plan_metadata, read by the run
  * calls of every layer) and of the per-call scratch (split partials) for a
  * batch of at most `max_batch` requests and `max_total_q` new-token rows.
- * Neither grows with the square of the sequence length.  Host pointers out. */
+ * Neither grows with the square of the sequence length.  Host pointers out.
+ * With split_target == 0 the DECODE sizes depend on the current device, so
+ * size, plan and run on the same device. */
 int pkv_workspace_size(const pkv_params* params, int32_t mode, int32_t max_batch,
                        int64_t max_total_q, size_t* workspace_bytes, size_t* scratch_bytes);
 
@@ -110,7 +114,9 @@ int pkv_workspace_size(const pkv_params* params, int32_t mode, int32_t max_batch
  * split-KV / query-tile work list into `workspace` (device, >=
  * workspace_bytes).  One kernel launch; the result is reused unchanged by
  * every layer's pkv_attn_* call with the same batch.  DECODE ignores
- * cu_seqlens_q (may be NULL) and total_q. */
+ * cu_seqlens_q (may be NULL) and total_q.  DECODE splits are the smallest
+ * that keep the work items within what the device runs at once, so a call
+ * runs in a single pass. */
 int pkv_plan_metadata(const pkv_params* params, int32_t mode, int32_t batch, int64_t total_q,
                       const int32_t* seq_lens, const int32_t* cu_seqlens_q, void* workspace,
                       size_t workspace_bytes, void* stream);

@@ -35,20 +35,21 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
   bounded only by the stated fp8 tolerance: parity unpinned beyond it.
 * ``plan_decode`` / ``plan_extend``: the split heuristic is a design choice,
   not from the pages; pinned by invariants (every token covered once, in
-  order; bounds on tile multiples; capacity; longest-first order).
+  order; bounds on tile multiples; capacity; the chunk is the smallest that
+  meets the item target; longest-first order when items overflow it).
 * ``kv_store``: pinned by a round trip.
 """
 from .attention import paged_attention
 from .merge import lse_merge
 from .e4m3 import e4m3_encode, e4m3_decode, E4M3_MAX
 from .sage import sage_decode
-from .plan import plan_decode, plan_extend, DECODE_TILE, EXTEND_BLOCK_M, DEFAULT_SPLIT_TARGET
+from .plan import plan_decode, plan_extend, decode_target_items, DECODE_TILE, EXTEND_BLOCK_M
 from .kv_store import kv_store
 from .memory import score_matrix_bytes
 
 __all__ = [
     "paged_attention", "lse_merge", "e4m3_encode",
     "e4m3_decode", "E4M3_MAX", "sage_decode", "plan_decode", "plan_extend",
-    "DECODE_TILE", "EXTEND_BLOCK_M", "DEFAULT_SPLIT_TARGET", "kv_store",
+    "DECODE_TILE", "EXTEND_BLOCK_M", "decode_target_items", "kv_store",
     "score_matrix_bytes",
 ]

@@ -129,14 +129,28 @@ def test_workspace_does_not_grow_with_square_of_length(lib):
 
 
 def test_capacity_matches_oracle_formula(lib):
-    from oracle.plan import decode_capacity, extend_capacity
-    for (hq, hkv, maxl, chunk, tgt, B) in [(32, 8, 4097, 0, 0, 64), (64, 8, 131073, 0, 0, 8),
-                                           (32, 8, 5000, 64, 0, 37), (40, 2, 700, 0, 64, 5)]:
+    from oracle.plan import decode_capacity, decode_target_items, extend_capacity
+    for (hq, hkv, maxl, chunk, tgt, B) in [(32, 8, 4097, 0, 4096, 64), (64, 8, 131073, 0, 4096, 8),
+                                           (32, 8, 5000, 64, 0, 37), (40, 2, 700, 0, 64, 5),
+                                           (32, 8, 4097, 0, 100, 64)]:
         p = pkv.Params(hq, hkv, 128, 16, maxl, kv_chunk=chunk, split_target=tgt)
         rc, ws, sc = _ws(lib, p, batch=B)
-        cap = decode_capacity(B, hkv, hq // hkv, maxl, chunk, tgt)
+        target = decode_target_items(hkv, hq // hkv, tgt, 1)
+        cap = decode_capacity(B, maxl, target, chunk)
         assert sc >= cap * hq * 129 * 4
         assert ws >= (16 + B + 1 + 4 * cap) * 4
     p = pkv.Params(32, 8, 128, 16, 4096)
     rc, ws, _ = _ws(lib, p, mode=pkv.PKV_EXTEND, batch=16, total_q=17000)
     assert ws >= 4 * (16 + 17 + 8 * extend_capacity(16, 17000, 4))
+
+
+def test_default_split_target_sizes_for_resident_waves(lib):
+    """Without a device the library sizes decode plans for 256 CUs x 16 resident
+    waves, the same as an explicit split_target of 4096 waves."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only fallback; a device reports its own occupancy")
+    for hq, hkv, B in ((32, 8, 64), (64, 8, 8), (40, 2, 5)):
+        p0 = pkv.Params(hq, hkv, 128, 16, 131073)
+        p1 = pkv.Params(hq, hkv, 128, 16, 131073, split_target=4096)
+        assert _ws(lib, p0, batch=B) == _ws(lib, p1, batch=B)

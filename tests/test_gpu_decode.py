@@ -177,7 +177,11 @@ def test_plan_matches_oracle_rederivation_bit_for_bit():
         plan = pkv.plan_metadata(params, pkv.PKV_DECODE, dev_i32(L))
         torch.cuda.synchronize()
         ws = plan.workspace.cpu().numpy().view(np.int32)
-        ref = oracle.plan_decode(L, 8, 4, max_kv, kv_chunk=kv_chunk, split_target=target)
+        if target:
+            assert ws[5] == oracle.decode_target_items(8, 4, target, 0)
+        else:
+            assert 1 <= ws[5]  # the device's resident items
+        ref = oracle.plan_decode(L, max_kv, int(ws[5]), kv_chunk=kv_chunk)
         n = ws[2]
         items_off = -(-(16 + B + 1) // 4) * 4
         items = ws[items_off:items_off + 4 * n].reshape(-1, 4)

@@ -104,13 +104,26 @@ def test_decode_plan_invariants(seed, kv_chunk):
     L = rng.integers(0, max_kv + 1, size=B)
     L[rng.integers(0, B)] = max_kv + 77  # beyond the bound: must be clamped
     Hkv, G = 8, int(rng.choice([1, 4, 8, 20]))
-    plan = oracle.plan_decode(L, Hkv, G, max_kv, kv_chunk=kv_chunk, split_target=int(rng.integers(1, 9000)))
+    target = oracle.decode_target_items(Hkv, G, int(rng.integers(1, 9000)), 512)
+    plan = oracle.plan_decode(L, max_kv, target, kv_chunk=kv_chunk)
     items = plan["items"]
     assert len(items) <= plan["capacity"]
     Lc = np.minimum(L, max_kv)
+    tiles = -(-Lc // oracle.DECODE_TILE)
     parts = []
     lengths = items[:, 2] - items[:, 1]
-    assert np.all(np.diff(lengths) <= 0)  # longest split first
+    if len(items) > target:
+        assert np.all(np.diff(lengths) <= 0)  # longest split first
+    else:
+        assert list(items[:, 0]) == sorted(items[:, 0])  # request order
+    if not kv_chunk:
+        count = lambda c: int(np.maximum(1, -(-tiles // c)).sum())
+        c = plan["chunk_tiles"]
+        assert len(items) == count(c)
+        # the chunk is the smallest meeting the target (or one item per request)
+        assert count(c) <= max(target, B)
+        if c > 1:
+            assert count(c - 1) > target
     for b in range(B):
         mine = items[items[:, 0] == b]
         mine = mine[np.argsort(mine[:, 1], kind="stable")]
