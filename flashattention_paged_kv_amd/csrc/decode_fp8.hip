@@ -36,34 +36,40 @@ __device__ __forceinline__ floatx4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, floatx4 
 struct Tile8 {
   u32x4 k[4][2];  // A operands of Sᵀ: 4 blocks of 16 keys, 32 bytes (channels 32j..32j+31)
   u32x2 v[16];    // the lane's 16 V rows, channels 8*(lane%16) .. +8
+  float ks[4];    // sfK of each 16-key block
 };
 
 // token (within the tile) of element e (0..15) held by lane group j in the Pᵀ / Vᵀ operands
 __device__ __forceinline__ int tok_of(int j, int e) { return 16 * (e >> 2) + 4 * j + (e & 3); }
 
-__device__ __forceinline__ int slot_at(const int32_t* __restrict__ rtt_row, int tok, int kv_end, int64_t pool_slots) {
-  return tok < kv_end ? clamp_slot(rtt_row[tok], pool_slots) : -1;
+// Slot of token t0 + (lane & 63), clamped to the item's last token: every
+// load is unconditional and positions past the range re-read a fetched row
+// (their scores are masked to -inf).
+__device__ __forceinline__ uint32_t slot_at(const int32_t* __restrict__ rtt_row, int t0, int kv_end, uint32_t last,
+                                            int lane) {
+  return clamp_slot_u32(rtt_row[min(t0 + lane, kv_end - 1)], last);
 }
 
-__device__ __forceinline__ void load_tile8(Tile8& t, int slot_a, int slot_b, const uint8_t* __restrict__ kbase,
-                                           const uint8_t* __restrict__ vbase, int64_t row_bytes, int lane) {
-  // slot_a: slot of token (lane & 63) of the tile, i.e. lanes hold tokens 0..63
+__device__ __forceinline__ void load_tile8(Tile8& t, uint32_t slot, int t0, int kv_end,
+                                           const float* __restrict__ sfk_row, int k_block,
+                                           const uint8_t* __restrict__ kbase, const uint8_t* __restrict__ vbase,
+                                           uint32_t row_bytes, int lane) {
+  // `slot`: slot of token (lane & 63) of the tile
   const int l16 = lane & 15, j = lane >> 4;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-  const u32x2 z2 = {0u, 0u};
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) t.ks[blk] = sfk_row[min(t0 + 16 * blk, kv_end - 1) / k_block];
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
-    const int sk = __shfl(slot_a, 16 * blk + l16);
-    const uint8_t* p = kbase + (int64_t)sk * row_bytes + 32 * j;
-    t.k[blk][0] = sk >= 0 ? ldg16(p) : z4;
-    t.k[blk][1] = sk >= 0 ? ldg16(p + 16) : z4;
+    const uint32_t sk = __shfl(slot, 16 * blk + l16);
+    const uint8_t* p = kbase + row_offset(sk, row_bytes) + 32 * j;
+    t.k[blk][0] = ldg16(p);
+    t.k[blk][1] = ldg16(p + 16);
   }
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int sv = __shfl(slot_a, tok_of(j, e));
-    t.v[e] = sv >= 0 ? ldg8(vbase + (int64_t)sv * row_bytes + 8 * l16) : z2;
+    const uint32_t sv = __shfl(slot, tok_of(j, e));
+    t.v[e] = ldg8(vbase + row_offset(sv, row_bytes) + 8 * l16);
   }
-  (void)slot_b;
 }
 
 // 4x4 byte transpose: out[c] = {x0.byte c, x1.byte c, x2.byte c, x3.byte c}
@@ -103,7 +109,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
   const int h = g * a.group + (head_ok ? hl : 0);
   const int row = a.rpi ? a.rpi[b] : b;
   const int32_t* __restrict__ rtt_row = a.rtt + (int64_t)row * a.rtt_stride;
-  const int64_t row_bytes = (int64_t)a.hkv * D;
+  const uint32_t row_bytes = (uint32_t)a.hkv * D;
   const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k_pool) + (int64_t)g * D;
   const uint8_t* __restrict__ vbase = static_cast<const uint8_t*>(a.v_pool) + (int64_t)g * D;
   const float* __restrict__ sfk_row = a.sfk + ((int64_t)b * a.hkv + g) * a.sfk_stride;
@@ -123,71 +129,86 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  auto compute = [&](const Tile8& cur, int t0) {
+    // ---- scores: 4 blocks of 16 keys; every 16-key block lies in one sfK block
+    float sc[16];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const i32x8 kop = {(int)cur.k[blk][0][0], (int)cur.k[blk][0][1], (int)cur.k[blk][0][2], (int)cur.k[blk][0][3],
+                         (int)cur.k[blk][1][0], (int)cur.k[blk][1][1], (int)cur.k[blk][1][2], (int)cur.k[blk][1][3]};
+      floatx4 s = {0.f, 0.f, 0.f, 0.f};
+      s = mfma_fp8_16x16x128(kop, qop, s);
+      const int tb = t0 + 16 * blk;
+      const float ks = cur.ks[blk] * qscale;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[4 * blk + r] = (tb + 4 * j + r < kv_end) ? s[r] * ks : kNegInf;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);  // finite: key t0 is in range
+    const float alpha = exp2_fast(m - m_new);
+    m = m_new;
+    float p[16];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = exp2_fast(sc[e] - m_new);
+      ps += p[e];
+    }
+    lpart = lpart * alpha + ps;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+    // P8ᵀ operand: element e (byte e) <-> key tok_of(j, e); bytes 16..31 are zero
+    i32x8 pop;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      pop[w] = (int)pack_fp8x4(448.f * p[4 * w], 448.f * p[4 * w + 1], 448.f * p[4 * w + 2], 448.f * p[4 * w + 3]);
+    pop[4] = pop[5] = pop[6] = pop[7] = 0;
+    // V8ᵀ operands: block c holds channel 8*l16 + c of the lane's 16 keys
+    uint32_t vt[8][4];  // [channel c][key group of 4]
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      uint32_t o_lo[4], o_hi[4];
+      transpose4x4(cur.v[4 * q4][0], cur.v[4 * q4 + 1][0], cur.v[4 * q4 + 2][0], cur.v[4 * q4 + 3][0], o_lo);
+      transpose4x4(cur.v[4 * q4][1], cur.v[4 * q4 + 1][1], cur.v[4 * q4 + 2][1], cur.v[4 * q4 + 3][1], o_hi);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        vt[c][q4] = o_lo[c];
+        vt[4 + c][q4] = o_hi[c];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const i32x8 vop = {(int)vt[c][0], (int)vt[c][1], (int)vt[c][2], (int)vt[c][3], 0, 0, 0, 0};
+      acc[c] = mfma_fp8_16x16x128(vop, pop, acc[c]);
+    }
+  };
+
   if (kv_begin < kv_end) {
-    Tile8 cur, nxt;
-    int slot_n = slot_at(rtt_row, kv_begin + lane, kv_end, a.pool_slots);
-    load_tile8(cur, slot_n, 0, kbase, vbase, row_bytes, lane);
-    slot_n = slot_at(rtt_row, kv_begin + kTile8 + lane, kv_end, a.pool_slots);
-    for (int t0 = kv_begin; t0 < kv_end; t0 += kTile8) {
-      const int slot_nn = slot_at(rtt_row, t0 + 2 * kTile8 + lane, kv_end, a.pool_slots);
-      load_tile8(nxt, slot_n, 0, kbase, vbase, row_bytes, lane);
-      // ---- scores: 4 blocks of 16 keys; every 16-key block lies in one sfK block
-      float sc[16];
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        const i32x8 kop = {(int)cur.k[blk][0][0], (int)cur.k[blk][0][1], (int)cur.k[blk][0][2], (int)cur.k[blk][0][3],
-                           (int)cur.k[blk][1][0], (int)cur.k[blk][1][1], (int)cur.k[blk][1][2], (int)cur.k[blk][1][3]};
-        floatx4 s = {0.f, 0.f, 0.f, 0.f};
-        s = mfma_fp8_16x16x128(kop, qop, s);
-        const int tb = t0 + 16 * blk;
-        const float ks = tb < kv_end ? sfk_row[tb / a.k_block] * qscale : 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[4 * blk + r] = (tb + 4 * j + r < kv_end) ? s[r] * ks : kNegInf;
-      }
-      float mx = sc[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);  // finite: key t0 is in range
-      const float alpha = exp2_fast(m - m_new);
-      m = m_new;
-      float p[16];
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = exp2_fast(sc[e] - m_new);
-        ps += p[e];
-      }
-      lpart = lpart * alpha + ps;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] *= alpha;
-      // P8ᵀ operand: element e (byte e) <-> key tok_of(j, e); bytes 16..31 are zero
-      i32x8 pop;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        pop[w] = (int)pack_fp8x4(448.f * p[4 * w], 448.f * p[4 * w + 1], 448.f * p[4 * w + 2], 448.f * p[4 * w + 3]);
-      pop[4] = pop[5] = pop[6] = pop[7] = 0;
-      // V8ᵀ operands: block c holds channel 8*l16 + c of the lane's 16 keys
-      uint32_t vt[8][4];  // [channel c][key group of 4]
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        uint32_t o_lo[4], o_hi[4];
-        transpose4x4(cur.v[4 * q4][0], cur.v[4 * q4 + 1][0], cur.v[4 * q4 + 2][0], cur.v[4 * q4 + 3][0], o_lo);
-        transpose4x4(cur.v[4 * q4][1], cur.v[4 * q4 + 1][1], cur.v[4 * q4 + 2][1], cur.v[4 * q4 + 3][1], o_hi);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          vt[c][q4] = o_lo[c];
-          vt[4 + c][q4] = o_hi[c];
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const i32x8 vop = {(int)vt[c][0], (int)vt[c][1], (int)vt[c][2], (int)vt[c][3], 0, 0, 0, 0};
-        acc[c] = mfma_fp8_16x16x128(vop, pop, acc[c]);
-      }
-      cur = nxt;
-      slot_n = slot_nn;
+    // Two register buffers in turn (as in the bf16 decode): while tile i is
+    // computed the rows of tile i+1 are in flight, and the slots of tile i+2
+    // were requested before them.
+    const uint32_t last = (uint32_t)(a.pool_slots - 1);
+    Tile8 ta, tb;
+    uint32_t s_odd, s_even = slot_at(rtt_row, kv_begin, kv_end, last, lane);
+    load_tile8(ta, s_even, kv_begin, kv_end, sfk_row, a.k_block, kbase, vbase, row_bytes, lane);
+    s_odd = slot_at(rtt_row, kv_begin + kTile8, kv_end, last, lane);
+    for (int t0 = kv_begin;;) {
+      s_even = slot_at(rtt_row, t0 + 2 * kTile8, kv_end, last, lane);
+      load_tile8(tb, s_odd, t0 + kTile8, kv_end, sfk_row, a.k_block, kbase, vbase, row_bytes, lane);
+      __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
+      compute(ta, t0);
+      t0 += kTile8;
+      if (t0 >= kv_end) break;
+      s_odd = slot_at(rtt_row, t0 + 2 * kTile8, kv_end, last, lane);
+      load_tile8(ta, s_even, t0 + kTile8, kv_end, sfk_row, a.k_block, kbase, vbase, row_bytes, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(tb, t0);
+      t0 += kTile8;
+      if (t0 >= kv_end) break;
     }
   }
 
