@@ -194,57 +194,97 @@ struct RowState {
   float m, lpart;
 };
 
-// One key tile: Sᵀ, mask, online softmax, Oᵀ.  The two 32-key halves keep
-// their own softmax step, so the VALU work of one half runs while the matrix
-// cores work on the other: QK of both halves is issued first, the softmax of
-// half 0 overlaps QK of half 1, the softmax of half 1 overlaps PV of half 0.
-template <int D>
+// One key tile: Sᵀ, mask, online softmax, Oᵀ, in two straight-line regions
+// around one (rarely taken) rescale branch:
+//  1. Sᵀ of both 32-key blocks (each block's MFMA chain in turn, the K
+//     operands read from LDS four MFMAs ahead), the Vᵀ operands of block 0,
+//     the tile's row max;
+//  2. exponentials of block 0, its PV product, the Vᵀ operands of block 1,
+//     exponentials of block 1 (overlapping block 0's PV), its PV product.
+// MASKED (diagonal tiles) applies the causal mask to the scores.
+template <int D, bool MASKED>
 __device__ __forceinline__ void compute_tile(RowState<D>& rs, const char* cur, const u32x4 (&qop)[D / 16],
                                              const int (&koff)[D / 16], const int (&vbase_off)[D / 32], int t0,
-                                             int pos, int wave_min_pos, float c, int lane) {
+                                             int pos, float c, int lane) {
   constexpr int QK_STEPS = D / 16;
   constexpr int DB = D / 32;
   const int jh = lane >> 5;
-  // ---- Sᵀ for two 32-key blocks (raw scores; the scale is folded in below)
+  const char* vt = cur + ExtSmem<D>::MAT;
+  // Vᵀ operands of a 32-key block: k-step ks2 = 2 kb + half covers keys
+  // 16 ks2 .. +16; this lane's 8 keys are {16 ks2 + 8 (e/4) + 4 jh + e%4}:
+  // two transposed 4-key reads per 32-channel block
+  auto read_v = [&](int kb, u32x4 (&vop)[2][DB]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int ks2 = 2 * kb + half;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 va = lds_read_tr16(vt + 16 * ks2 * ExtSmem<D>::RB, vbase_off[db]);
+        const u32x2 vb = lds_read_tr16(vt + (16 * ks2 + 8) * ExtSmem<D>::RB, vbase_off[db]);
+        vop[half][db] = u32x4{va[0], va[1], vb[0], vb[1]};
+      }
+    }
+  };
+  // ---- region 1: Sᵀ (raw scores; the scale is folded in below)
   floatx16 s[2];
+  u32x4 vop0[2][DB];
+  {
+    u32x4 kop[2][QK_STEPS];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int ks = 0; ks < QK_STEPS; ++ks)
+        kop[kb][ks] = *reinterpret_cast<const u32x4*>(cur + 32 * kb * ExtSmem<D>::RB + koff[ks]);
 #pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ++ks) {
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(cur + 32 * kb * ExtSmem<D>::RB + koff[ks]);
-      s[kb] = mfma32x32x16(as_bf16x8(kv), as_bf16x8(qop[ks]), s[kb]);
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < QK_STEPS; ++ks) s[kb] = mfma32x32x16(as_bf16x8(kop[kb][ks]), as_bf16x8(qop[ks]), s[kb]);
+    }
+    read_v(0, vop0);
+    // 2 QK_STEPS K reads and 4 DB V reads (as 2 DB pairs) around 2 QK_STEPS MFMAs:
+    // four reads ahead, then one read after each MFMA, the V reads last
+    constexpr int NK = 2 * QK_STEPS, NV = 4 * DB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NK - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NV / 4, 0);
     }
   }
-  const bool masked = t0 + kBN - 1 > wave_min_pos;  // the tile crosses some row's diagonal
-  const char* vt = cur + ExtSmem<D>::MAT;
+  if (MASKED) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    if (masked) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * jh + (r & 3);
         s[kb][r] = key <= pos ? s[kb][r] : kNegInf;
       }
-    }
-    float mx = s[kb][0];
+  }
+  float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-    // lazy rescale: the reference max moves only when a row's max exceeds it by
-    // more than 8 (log2 units), so exp2(s - m) <= 256 while acc and l keep
-    // referring to the same m
-    if (__any(mx > rs.m + 8.f)) {
-      const float m_new = fmaxf(rs.m, mx);
-      const float alpha = m_new == kNegInf ? 1.f : exp2_fast(rs.m - m_new);
-      rs.lpart *= alpha;
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+  // lazy rescale: the reference max moves only when a row's max exceeds it by
+  // more than 8 (log2 units), so exp2(s - m) <= 256 while acc and l keep
+  // referring to the same m
+  if (__any(mx > rs.m + 8.f)) {
+    const float m_new = fmaxf(rs.m, mx);
+    const float alpha = m_new == kNegInf ? 1.f : exp2_fast(rs.m - m_new);
+    rs.lpart *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) rs.acc[db] *= alpha;
-      rs.m = m_new;
-    }
-    const float m_use = rs.m == kNegInf ? 0.f : rs.m;
-    u32x4 pop[2];  // Pᵀ B operands of the half's two 16-key k-steps
+    for (int db = 0; db < DB; ++db) rs.acc[db] *= alpha;
+    rs.m = m_new;
+  }
+  // ---- region 2
+  const float m_use = rs.m == kNegInf ? 0.f : rs.m;
+  auto exp_block = [&](int kb, u32x4 (&pop)[2]) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       float pv[8];
@@ -256,20 +296,21 @@ __device__ __forceinline__ void compute_tile(RowState<D>& rs, const char* cur, c
         rs.lpart += pv[2 * w] + pv[2 * w + 1];
       }
     }
-    // Oᵀ += Vᵀ·Pᵀ.  k-step ks2 covers keys 16 ks2 .. +16; this lane's 8 keys are
-    // {16 ks2 + 8 (e/4) + 4 jh + e%4}: two transposed 4-key reads
+  };
+  auto pv_block = [&](const u32x4 (&pop)[2], const u32x4 (&vop)[2][DB]) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int ks2 = 2 * kb + half;
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x2 va = lds_read_tr16(vt + 16 * ks2 * ExtSmem<D>::RB, vbase_off[db]);
-        const u32x2 vb = lds_read_tr16(vt + (16 * ks2 + 8) * ExtSmem<D>::RB, vbase_off[db]);
-        u32x4 vop = {va[0], va[1], vb[0], vb[1]};
-        rs.acc[db] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(pop[half]), rs.acc[db]);
-      }
-    }
-  }
+      for (int db = 0; db < DB; ++db)
+        rs.acc[db] = mfma32x32x16(as_bf16x8(vop[half][db]), as_bf16x8(pop[half]), rs.acc[db]);
+  };
+  u32x4 pop0[2], pop1[2];
+  exp_block(0, pop0);
+  pv_block(pop0, vop0);
+  u32x4 vop1[2][DB];
+  read_v(1, vop1);
+  exp_block(1, pop1);
+  pv_block(pop1, vop1);
 }
 
 }  // namespace
@@ -378,7 +419,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (wave == 0 && tile + 3 < ntiles) issue_slots(rtt_row, t0 + 3 * kBN, kv_end, slot0 + J * S::SLOT_BYTES, lane);
     const bool kv2 = tile + 2 < ntiles;
     if (kv2) issue_kv<D>(slot0 + J2 * S::SLOT_BYTES, kv0 + J2 * S::STAGE, kbase, vbase, row_elems, last_slot, wave, lane);
-    if (t0 <= wave_max_pos) compute_tile<D>(rs, kv0 + J * S::STAGE, qop, ko, vbo, t0, pos, wave_min_pos, c, lane);
+    if (t0 <= wave_max_pos) {
+      if (t0 + kBN - 1 > wave_min_pos)  // the tile crosses some row's diagonal
+        compute_tile<D, true>(rs, kv0 + J * S::STAGE, qop, ko, vbo, t0, pos, c, lane);
+      else
+        compute_tile<D, false>(rs, kv0 + J * S::STAGE, qop, ko, vbo, t0, pos, c, lane);
+    }
     // publish tile+1 and the slots of tile+3: all but tile+2's K/V loads have landed
     if (kv2) wait_vmem<2 * S::NQ>(); else wait_vmem<0>();
     if (tile + 1 < ntiles) zero_rows_past_end<D>(kv0 + J1 * S::STAGE, t0 + kBN, kv_end, wave, lane);
