@@ -13,14 +13,15 @@
 // workgroup fills a CU (two waves per SIMD).
 //
 // Data movement is asynchronous and register-free: global -> LDS loads
-// (gfx950 global_load_lds_*) fill a ring of three K/V stages and three slot
-// stages.  While tile t is computed, the K/V rows of tile t+2 and the
-// req_to_token entries of tile t+3 are in flight; the slots of a tile are
-// read from LDS one step before its K/V rows are requested.  The tile loop is
-// unrolled by the ring period (3), so every LDS address is a per-lane offset
-// computed once plus an immediate.
+// (gfx950 global_load_lds_*) fill a ring of two 128-key K/V stages and a
+// ring of three req_to_token stages.  While tile t is computed (as two
+// 64-key halves), the K/V rows of tile t+1 and the req_to_token entries of
+// tile t+2 are in flight; the loads are issued between the first MFMAs of the
+// tile so their address work hides under the matrix cores.  The tile loop is
+// unrolled by the K/V ring period (2), so every LDS address is a per-lane
+// offset computed once plus an immediate.
 //
-// Per wave and key tile, with 32x32x16 bf16 MFMAs:
+// Per wave and 64-key half tile, with 32x32x16 bf16 MFMAs:
 //  * Sᵀ = K·Qᵀ: K rows from LDS are the A operand (16-byte reads), the
 //    wave's Q rows the B operand (registers).  The Sᵀ layout gives each lane
 //    ONE row and 16 keys of every 32-key block, so the row max / sum are
@@ -41,14 +42,18 @@ namespace pkv {
 
 namespace {
 
-constexpr int kBN = kExtendTileN;         // keys per tile (64)
+constexpr int kBN = 2 * kExtendTileN;     // keys per tile (128), computed in halves of 64
+constexpr int kHalf = kExtendTileN;
 constexpr int kWaves = kExtendRows / 32;  // 8 waves x 32 rows
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKVStages = 3;
-constexpr int kSlotStages = 3;  // same period as the K/V ring: stage indices are static
+constexpr int kKVStages = 2;
+constexpr int kSlotStages = 3;  // req_to_token entries are requested 2 tiles ahead (indexed at run time)
 
-// One K/V stage: a K tile then a V tile, rows of D*2 bytes, unpadded, with the
-// 16-byte chunks of each row XOR-swizzled against bank conflicts:
+// LDS holds the K tiles of all stages, then the V tiles of all stages, then
+// the slot stages, so a tile's K (or V) rows sit at a per-lane offset plus an
+// immediate below 64 KiB for every stage (DS instructions take a 16-bit
+// offset).  Rows are D*2 bytes, unpadded, with the 16-byte chunks of each row
+// XOR-swizzled against bank conflicts:
 //  * K: chunk c of key r at position c ^ (r % CH) -- the 16-byte row reads of
 //    the Sᵀ product touch one chunk of many consecutive keys;
 //  * V: chunk c of key r at position c ^ (2 (r % 8) % CH) -- each transpose
@@ -59,11 +64,12 @@ struct ExtSmem {
   static constexpr int RB = D * 2;                        // bytes per key row
   static constexpr int CH = D / 8;                        // 16-byte chunks per row
   static constexpr int MAT = kBN * RB;                    // one matrix tile
-  static constexpr int STAGE = 2 * MAT;                   // K then V
+  static constexpr int STAGE = MAT;                       // stride between stages' K (or V) tiles
+  static constexpr int VOFF = kKVStages * MAT;            // a stage's V tile, from its K tile
   static constexpr int ROWS_PER_KB = 1024 / RB;           // rows written by one 64-lane 16-byte load
   static constexpr int NQ = kBN / ROWS_PER_KB / kWaves;   // such loads per wave and matrix
   static constexpr int SLOT_BYTES = kBN * 4;              // req_to_token entries of one tile
-  static constexpr int TOTAL = kKVStages * STAGE + kSlotStages * SLOT_BYTES;
+  static constexpr int TOTAL = 2 * kKVStages * MAT + kSlotStages * SLOT_BYTES;
 };
 
 template <int D>
@@ -111,10 +117,8 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
 }
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else static_assert(N == 0 || N == 2 || N == 4, "unsupported wait depth");
+  static_assert(N >= 0 && N <= 15, "vmcnt wait depth");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Row of the tile handled by (wave, load q, lane); the lane writes LDS chunk
@@ -125,21 +129,38 @@ __device__ __forceinline__ int tile_row(int wave, int q, int lane) {
   return (wave * ExtSmem<D>::NQ + q) * ExtSmem<D>::ROWS_PER_KB + lane / ExtSmem<D>::CH;
 }
 
-// K and V rows of one tile into a stage, from the slots in a slot stage.
+// K and V rows of one tile into a stage, from the slots in a slot stage, in
+// two halves: read_kv_slots fetches this lane's slots from LDS, issue_kv_rows
+// starts the global -> LDS row loads (so the LDS latency of the first can be
+// hidden behind other work).
 template <int D>
-__device__ __forceinline__ void issue_kv(const char* slots, char* stage, const uint16_t* __restrict__ kbase,
-                                         const uint16_t* __restrict__ vbase, uint32_t row_elems,
-                                         uint32_t last_slot, int wave, int lane) {
+__device__ __forceinline__ void read_kv_slots(const char* slots, int wave, int lane, int (&sv)[ExtSmem<D>::NQ]) {
+#pragma unroll
+  for (int q = 0; q < ExtSmem<D>::NQ; ++q) sv[q] = *reinterpret_cast<const int*>(slots + 4 * tile_row<D>(wave, q, lane));
+}
+
+template <int D>
+__device__ __forceinline__ void issue_kv_rows(const int (&sv)[ExtSmem<D>::NQ], char* stage,
+                                              const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
+                                              uint32_t row_elems, uint32_t last_slot, int wave, int lane) {
   const int p = lane % ExtSmem<D>::CH;
 #pragma unroll
   for (int q = 0; q < ExtSmem<D>::NQ; ++q) {
     const int r = tile_row<D>(wave, q, lane);
-    const int s = *reinterpret_cast<const int*>(slots + 4 * r);
-    const int64_t row_off = row_offset(clamp_slot_u32(s, last_slot), row_elems);
+    const int64_t row_off = row_offset(clamp_slot_u32(sv[q], last_slot), row_elems);
     const uint32_t dst = lds_addr(stage) + (wave * ExtSmem<D>::NQ + q) * 1024;
     dma16(kbase + row_off + 8 * (p ^ swz_k<D>(r)), dst);
-    dma16(vbase + row_off + 8 * (p ^ swz_v<D>(r)), dst + ExtSmem<D>::MAT);
+    dma16(vbase + row_off + 8 * (p ^ swz_v<D>(r)), dst + ExtSmem<D>::VOFF);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void issue_kv(const char* slots, char* stage, const uint16_t* __restrict__ kbase,
+                                         const uint16_t* __restrict__ vbase, uint32_t row_elems,
+                                         uint32_t last_slot, int wave, int lane) {
+  int sv[ExtSmem<D>::NQ];
+  read_kv_slots<D>(slots, wave, lane, sv);
+  issue_kv_rows<D>(sv, stage, kbase, vbase, row_elems, last_slot, wave, lane);
 }
 
 // req_to_token entries of the 64 keys of a tile (one wave; keys past kv_end
@@ -147,6 +168,7 @@ __device__ __forceinline__ void issue_kv(const char* slots, char* stage, const u
 __device__ __forceinline__ void issue_slots(const int32_t* __restrict__ rtt_row, int t0, int kv_end,
                                             char* slot_stage, int lane) {
   dma4(rtt_row + min(t0 + lane, kv_end - 1), lds_addr(slot_stage));
+  dma4(rtt_row + min(t0 + 64 + lane, kv_end - 1), lds_addr(slot_stage) + 256);
 }
 
 // Rows past kv_end that this lane fetched are overwritten with zeros once its
@@ -160,7 +182,7 @@ __device__ __forceinline__ void zero_rows_past_end(char* stage, int t0, int kv_e
     if (t0 + tile_row<D>(wave, q, lane) >= kv_end) {
       char* dst = stage + (wave * ExtSmem<D>::NQ + q) * 1024 + 16 * lane;
       *reinterpret_cast<u32x4*>(dst) = z;
-      *reinterpret_cast<u32x4*>(dst + ExtSmem<D>::MAT) = z;
+      *reinterpret_cast<u32x4*>(dst + ExtSmem<D>::VOFF) = z;
     }
   }
 }
@@ -194,69 +216,42 @@ struct RowState {
   float m, lpart;
 };
 
-// One key tile: Sᵀ, mask, online softmax, Oᵀ, in two straight-line regions
-// around one (rarely taken) rescale branch:
-//  1. Sᵀ of both 32-key blocks (each block's MFMA chain in turn, the K
-//     operands read from LDS four MFMAs ahead), the Vᵀ operands of block 0,
-//     the tile's row max;
-//  2. exponentials of block 0, its PV product, the Vᵀ operands of block 1,
-//     exponentials of block 1 (overlapping block 0's PV), its PV product.
-// MASKED (diagonal tiles) applies the causal mask to the scores.
-template <int D, bool MASKED>
-__device__ __forceinline__ void compute_tile(RowState<D>& rs, const char* cur, const u32x4 (&qop)[D / 16],
-                                             const int (&koff)[D / 16], const int (&vbase_off)[D / 32], int t0,
-                                             int pos, float c, int lane) {
+// One key tile in two parts.  qk_tile: Sᵀ of both 32-key blocks (each
+// block's MFMA chain in turn, K operands read from LDS four MFMAs ahead), the
+// causal mask on diagonal tiles (MASKED), the tile's row max, the lazy
+// rescale and the exponentials, leaving the tile's probabilities as the bf16
+// Pᵀ operands `pop` (k-step ks2 = 2 kb + half); `mid` runs between the first
+// MFMAs (the step's global -> LDS loads are issued there).  pv_tile: Oᵀ += Vᵀ·Pᵀ.
+template <int D, bool MASKED, typename Mid>
+__device__ __forceinline__ void qk_tile(RowState<D>& rs, u32x4 (&pop)[4], const char* cur,
+                                        const u32x4 (&qop)[D / 16], const int (&koff)[D / 16], int t0, int pos,
+                                        float c, int lane, Mid&& mid) {
   constexpr int QK_STEPS = D / 16;
   constexpr int DB = D / 32;
   const int jh = lane >> 5;
-  const char* vt = cur + ExtSmem<D>::MAT;
-  // Vᵀ operands of a 32-key block: k-step ks2 = 2 kb + half covers keys
-  // 16 ks2 .. +16; this lane's 8 keys are {16 ks2 + 8 (e/4) + 4 jh + e%4}:
-  // two transposed 4-key reads per 32-channel block
-  auto read_v = [&](int kb, u32x4 (&vop)[2][DB]) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int ks2 = 2 * kb + half;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x2 va = lds_read_tr16(vt + 16 * ks2 * ExtSmem<D>::RB, vbase_off[db]);
-        const u32x2 vb = lds_read_tr16(vt + (16 * ks2 + 8) * ExtSmem<D>::RB, vbase_off[db]);
-        vop[half][db] = u32x4{va[0], va[1], vb[0], vb[1]};
-      }
-    }
-  };
-  // ---- region 1: Sᵀ (raw scores; the scale is folded in below)
   floatx16 s[2];
-  u32x4 vop0[2][DB];
   {
-    u32x4 kop[2][QK_STEPS];
+    // K operand n = QK_STEPS kb + ks is read four MFMAs before its use; the
+    // sched_barriers keep exactly that order (and the register window small)
+    constexpr int NK = 2 * QK_STEPS, AHEAD = 4;
+    auto kread = [&](int n) {
+      return *reinterpret_cast<const u32x4*>(cur + 32 * (n / QK_STEPS) * ExtSmem<D>::RB + koff[n % QK_STEPS]);
+    };
+    u32x4 kop[NK];
+#pragma unroll
+    for (int n = 0; n < AHEAD; ++n) kop[n] = kread(n);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks)
-        kop[kb][ks] = *reinterpret_cast<const u32x4*>(cur + 32 * kb * ExtSmem<D>::RB + koff[ks]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) s[kb] = mfma32x32x16(as_bf16x8(kop[kb][ks]), as_bf16x8(qop[ks]), s[kb]);
+    for (int n = 0; n < NK; ++n) {
+      __builtin_amdgcn_sched_barrier(0);
+      s[n / QK_STEPS] = mfma32x32x16(as_bf16x8(kop[n]), as_bf16x8(qop[n % QK_STEPS]), s[n / QK_STEPS]);
+      if (n + AHEAD < NK) kop[n + AHEAD] = kread(n + AHEAD);
+      if (n == AHEAD) mid();  // the caller's loads start under the MFMAs
     }
-    read_v(0, vop0);
-    // 2 QK_STEPS K reads and 4 DB V reads (as 2 DB pairs) around 2 QK_STEPS MFMAs:
-    // four reads ahead, then one read after each MFMA, the V reads last
-    constexpr int NK = 2 * QK_STEPS, NV = 4 * DB;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < NK - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, NV / 4, 0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (MASKED) {
 #pragma unroll
@@ -282,35 +277,47 @@ __device__ __forceinline__ void compute_tile(RowState<D>& rs, const char* cur, c
     for (int db = 0; db < DB; ++db) rs.acc[db] *= alpha;
     rs.m = m_new;
   }
-  // ---- region 2
   const float m_use = rs.m == kNegInf ? 0.f : rs.m;
-  auto exp_block = [&](int kb, u32x4 (&pop)[2]) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float pv[8];
+  for (int ks2 = 0; ks2 < 4; ++ks2) {
+    float pv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[kb][8 * half + e], c, -m_use));
+    for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[ks2 >> 1][8 * (ks2 & 1) + e], c, -m_use));
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        pop[half][w] = pack_bf16x2(pv[2 * w], pv[2 * w + 1]);
-        rs.lpart += pv[2 * w] + pv[2 * w + 1];
-      }
+    for (int w = 0; w < 4; ++w) {
+      pop[ks2][w] = pack_bf16x2(pv[2 * w], pv[2 * w + 1]);
+      rs.lpart += pv[2 * w] + pv[2 * w + 1];
     }
+  }
+}
+
+// Oᵀ += Vᵀ·Pᵀ over the tile's 4 key steps.  Step ks2 covers keys 16 ks2 ..
+// +16; this lane's 8 keys are {16 ks2 + 8 (e/4) + 4 jh + e%4}: two transposed
+// 4-key reads per 32-channel block, read one step ahead.
+template <int D>
+__device__ __forceinline__ void pv_tile(RowState<D>& rs, const u32x4 (&pop)[4], const char* cur,
+                                        const int (&vbase_off)[D / 32]) {
+  constexpr int DB = D / 32;
+  const char* vt = cur + ExtSmem<D>::VOFF;
+  // operands of MFMA n = DB ks2 + db are read one key step (DB MFMAs) ahead;
+  // the sched_barriers keep that order
+  constexpr int NM = 4 * DB;
+  auto vread = [&](int n) {
+    const int ks2 = n / DB, db = n % DB;
+    const u32x2 va = lds_read_tr16(vt + 16 * ks2 * ExtSmem<D>::RB, vbase_off[db]);
+    const u32x2 vb = lds_read_tr16(vt + (16 * ks2 + 8) * ExtSmem<D>::RB, vbase_off[db]);
+    return u32x4{va[0], va[1], vb[0], vb[1]};
   };
-  auto pv_block = [&](const u32x4 (&pop)[2], const u32x4 (&vop)[2][DB]) {
+  u32x4 vop[NM];
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
+  for (int n = 0; n < DB; ++n) vop[n] = vread(n);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        rs.acc[db] = mfma32x32x16(as_bf16x8(vop[half][db]), as_bf16x8(pop[half]), rs.acc[db]);
-  };
-  u32x4 pop0[2], pop1[2];
-  exp_block(0, pop0);
-  pv_block(pop0, vop0);
-  u32x4 vop1[2][DB];
-  read_v(1, vop1);
-  exp_block(1, pop1);
-  pv_block(pop1, vop1);
+  for (int n = 0; n < NM; ++n) {
+    __builtin_amdgcn_sched_barrier(0);
+    rs.acc[n % DB] = mfma32x32x16(as_bf16x8(vop[n]), as_bf16x8(pop[n / DB]), rs.acc[n % DB]);
+    if (n + DB < NM) vop[n + DB] = vread(n + DB);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace
@@ -387,53 +394,69 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   int ko[QK_STEPS];
   k_read_offsets<D>(ko, lane);
-  char* const kv0 = smem;  // three K/V stages, then three slot stages
-  char* const slot0 = smem + kKVStages * S::STAGE;
+  char* const kv0 = smem;  // K tile of stage J at kv0 + J * STAGE, its V tile VOFF further
+  char* const slot0 = smem + 2 * kKVStages * S::MAT;
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
-  // prologue: slots of tiles 0..2 (wave 0), then K/V of tiles 0 and 1
+  // Tile u's req_to_token entries go to slot stage u % 3 (requested by wave 0
+  // at step u-2), its K/V rows to stage u % 2 (requested at step u-1).  Each
+  // step ends with all of its own loads landed (tile t+1 and the entries of
+  // tile t+2) before the barrier publishes them.
+  auto slot_stage = [&](int u) { return slot0 + (u % kSlotStages) * S::SLOT_BYTES; };
+  // prologue: entries of tiles 0 and 1, then the K/V rows of tile 0
   if (ntiles > 0) {
     if (wave == 0) {
-      for (int t = 0; t < 3 && t < ntiles; ++t) issue_slots(rtt_row, t * kBN, kv_end, slot0 + t * S::SLOT_BYTES, lane);
+      for (int t = 0; t < 2 && t < ntiles; ++t) issue_slots(rtt_row, t * kBN, kv_end, slot_stage(t), lane);
       wait_vmem<0>();
     }
     __syncthreads();
-    issue_kv<D>(slot0, kv0, kbase, vbase, row_elems, last_slot, wave, lane);
-    if (ntiles > 1) {
-      issue_kv<D>(slot0 + S::SLOT_BYTES, kv0 + S::STAGE, kbase, vbase, row_elems, last_slot, wave, lane);
-      wait_vmem<2 * S::NQ>();  // tile 0 lands, tile 1 may stay in flight
-    } else {
-      wait_vmem<0>();
-    }
+    issue_kv<D>(slot_stage(0), kv0, kbase, vbase, row_elems, last_slot, wave, lane);
+    wait_vmem<0>();
     zero_rows_past_end<D>(kv0, 0, kv_end, wave, lane);
   }
   __syncthreads();
-
-  // One step over tile `tile` whose ring index is J = tile % 3 (compile time).
-  auto step = [&](int tile, auto J_) {
+  auto qk = [&](int t0, const char* stage, u32x4 (&pop)[4], auto&& mid) __attribute__((always_inline)) {
+    if (t0 + kHalf - 1 > wave_min_pos)
+      qk_tile<D, true>(rs, pop, stage, qop, ko, t0, pos, c, lane, mid);
+    else
+      qk_tile<D, false>(rs, pop, stage, qop, ko, t0, pos, c, lane, mid);
+  };
+  auto nothing = [&]() __attribute__((always_inline)) {};
+  // One step over 128-key tile `tile` (K/V stage J = tile % 2, compile time):
+  // read the slots of tile+1 from LDS, compute the first 64-key half with the
+  // loads of the entries of tile+2 and the rows of tile+1 issued between its
+  // first MFMAs, then the second half (skipped when causally invisible).
+  auto step = [&](int tile, auto J_) __attribute__((always_inline)) {
     constexpr int J = decltype(J_)::value;
-    constexpr int J1 = (J + 1) % 3, J2 = (J + 2) % 3;
+    constexpr int J1 = (J + 1) % 2;
     const int t0 = tile * kBN;
-    // slots of tile+3 (wave 0; ring index J), then the K/V rows of tile+2: both
-    // are in flight while tiles tile and tile+1 are computed
-    if (wave == 0 && tile + 3 < ntiles) issue_slots(rtt_row, t0 + 3 * kBN, kv_end, slot0 + J * S::SLOT_BYTES, lane);
-    const bool kv2 = tile + 2 < ntiles;
-    if (kv2) issue_kv<D>(slot0 + J2 * S::SLOT_BYTES, kv0 + J2 * S::STAGE, kbase, vbase, row_elems, last_slot, wave, lane);
+    const bool sl2 = wave == 0 && tile + 2 < ntiles;
+    const bool kv1 = tile + 1 < ntiles;
+    int sv[S::NQ];
+    if (kv1) read_kv_slots<D>(slot_stage(tile + 1), wave, lane, sv);
+    auto loads = [&]() __attribute__((always_inline)) {
+      if (sl2) issue_slots(rtt_row, t0 + 2 * kBN, kv_end, slot_stage(tile + 2), lane);
+      if (kv1) issue_kv_rows<D>(sv, kv0 + J1 * S::STAGE, kbase, vbase, row_elems, last_slot, wave, lane);
+    };
     if (t0 <= wave_max_pos) {
-      if (t0 + kBN - 1 > wave_min_pos)  // the tile crosses some row's diagonal
-        compute_tile<D, true>(rs, kv0 + J * S::STAGE, qop, ko, vbo, t0, pos, c, lane);
-      else
-        compute_tile<D, false>(rs, kv0 + J * S::STAGE, qop, ko, vbo, t0, pos, c, lane);
+      u32x4 pop[4];
+      qk(t0, kv0 + J * S::STAGE, pop, loads);
+      pv_tile<D>(rs, pop, kv0 + J * S::STAGE, vbo);
+      if (t0 + kHalf <= wave_max_pos) {
+        u32x4 pop2[4];
+        qk(t0 + kHalf, kv0 + J * S::STAGE + kHalf * S::RB, pop2, nothing);
+        pv_tile<D>(rs, pop2, kv0 + J * S::STAGE + kHalf * S::RB, vbo);
+      }
+    } else {
+      loads();
     }
-    // publish tile+1 and the slots of tile+3: all but tile+2's K/V loads have landed
-    if (kv2) wait_vmem<2 * S::NQ>(); else wait_vmem<0>();
-    if (tile + 1 < ntiles) zero_rows_past_end<D>(kv0 + J1 * S::STAGE, t0 + kBN, kv_end, wave, lane);
+    wait_vmem<0>();
+    if (kv1) zero_rows_past_end<D>(kv0 + J1 * S::STAGE, t0 + kBN, kv_end, wave, lane);
     __syncthreads();
   };
-  for (int tile = 0; tile < ntiles; tile += 3) {
+  for (int tile = 0; tile < ntiles; tile += 2) {
     step(tile, std::integral_constant<int, 0>());
     if (tile + 1 < ntiles) step(tile + 1, std::integral_constant<int, 1>());
-    if (tile + 2 < ntiles) step(tile + 2, std::integral_constant<int, 2>());
   }
   wait_vmem<0>();
 
