@@ -330,10 +330,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ __attribute__((aligned(1024))) char smem[S::TOTAL];
 
   const int32_t* __restrict__ ws = a.ws;
-  if ((int)blockIdx.x >= ws[WS_NUM_ITEMS]) return;
-  const int4 it = reinterpret_cast<const int4*>(ws + a.items_off)[blockIdx.x];
+  // 1-D grid, workgroup = item * Hkv + kv head: workgroups go to the 8 XCDs
+  // round-robin, so with Hkv a multiple of 8 each XCD serves one kv head for
+  // all items and the query tiles that re-read a head's K/V rows share its L2
+  const int xi = (int)blockIdx.x / a.hkv;
+  if (xi >= ws[WS_NUM_ITEMS]) return;
+  const int4 it = reinterpret_cast<const int4*>(ws + a.items_off)[xi];
   const int b = it.x, qt = it.y, kv_end = it.z;
-  const int g = blockIdx.y;
+  const int g = (int)blockIdx.x - xi * a.hkv;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS targets on the scalar unit
   const int l32 = lane & 31, jh = lane >> 5;
@@ -480,7 +484,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
 hipError_t launch_extend_bf16(const ExtendArgs& a, int head_dim, int64_t capacity, hipStream_t s) {
   if (capacity <= 0) return hipSuccess;
-  dim3 grid((unsigned)capacity, (unsigned)a.hkv);
+  dim3 grid((unsigned)(capacity * a.hkv));
   if (head_dim == 128) hipLaunchKernelGGL(extend_bf16_kernel<128>, grid, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(extend_bf16_kernel<64>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();

@@ -284,6 +284,9 @@ int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void*
   if ((int64_t)workspace_bytes < w.total_ints * 4)
     return fail(PKV_EWORKSPACE, "workspace_bytes=%zu is smaller than the %lld bytes required", workspace_bytes,
                 (long long)(w.total_ints * 4));
+  if (w.capacity * params->num_kv_heads > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "extend work items x kv heads (%lld) exceed the grid limit",
+                (long long)(w.capacity * params->num_kv_heads));
   pkv::ExtendArgs a{};
   a.q = q;
   a.k_pool = k_pool;
