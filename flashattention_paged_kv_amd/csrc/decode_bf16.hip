@@ -21,6 +21,7 @@
 // normalised partial O and log2-sum-exp go to scratch and the merge kernel
 // (decode_merge.h) combines them.
 #include "decode_merge.h"
+#include "decode_stream.h"
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -121,68 +122,24 @@ __device__ __forceinline__ void compute_tile(const KVTile<D>& t, const u32x4 (&q
 
 }  // namespace
 
-// WPB waves per workgroup take WPB consecutive (kv head, head group) units of
-// the same split, so the rows of one token are requested together.
-template <int D, int WPB>
-__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(DecodeArgs a) {
-  constexpr int KB = D / 32;
-  const int32_t* __restrict__ ws = a.ws;
-  if ((int)blockIdx.x >= ws[WS_NUM_ITEMS]) return;
-  const int unit = blockIdx.y * WPB + (threadIdx.x >> 6);
-  if (unit >= a.hkv * a.head_groups) return;
-  const int4 it = reinterpret_cast<const int4*>(ws + a.items_off)[blockIdx.x];
-  const int b = it.x, kv_begin = it.y, kv_end = it.z, part = it.w;
-  const int g = unit / a.head_groups, hg = unit - g * a.head_groups;
-  const int lane = threadIdx.x & 63;
-  const int l16 = lane & 15, j = lane >> 4;
-  const int hl = hg * 16 + l16;
-  const bool head_ok = hl < a.group;
-  const int h = g * a.group + hl;
-  const int row = a.rpi ? a.rpi[b] : b;
-  const int32_t* __restrict__ rtt_row = a.rtt + (int64_t)row * a.rtt_stride;
-  const uint32_t row_elems = (uint32_t)a.hkv * D;
-  const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * D;
-  const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * D;
-
-  u32x4 qop[KB];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (head_ok ? h : 0)) * D;
-    const u32x4 z = {0u, 0u, 0u, 0u};
+template <int D>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, u32x4 (&qop)[D / 32], int b, int h, bool head_ok,
+                                       int j) {
+  h = opaque(h);
+  j = opaque(j);
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (head_ok ? h : 0)) * D;
+  const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qop[kb] = head_ok ? ldg16(qrow + 32 * kb + 8 * j) : z;
-  }
+  for (int kb = 0; kb < D / 32; ++kb) qop[kb] = head_ok ? ldg16(qrow + 32 * kb + 8 * j) : z;
+}
 
-  float m = kNegInf, lpart = 0.f;
-  floatx4 acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  if (kv_begin < kv_end) {
-    // Software pipeline over 32-token tiles, two register buffers used in
-    // turn: while tile i is computed, the K/V rows of tile i+1 are in flight
-    // and the slots of tile i+2 were requested before them, so waiting for a
-    // slot never waits for the K/V rows issued after it.
-    const uint32_t last = (uint32_t)(a.pool_slots - 1);
-    KVTile<D> ta, tb;
-    uint32_t s_odd, s_even = tile_slot(rtt_row, kv_begin, kv_end, last, lane);
-    load_tile<D>(ta, s_even, kbase, vbase, row_elems, lane);
-    s_odd = tile_slot(rtt_row, kv_begin + kDecodeTile, kv_end, last, lane);
-    for (int t0 = kv_begin;;) {
-      s_even = tile_slot(rtt_row, t0 + 2 * kDecodeTile, kv_end, last, lane);
-      load_tile<D>(tb, s_odd, kbase, vbase, row_elems, lane);
-      __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
-      compute_tile<D>(ta, qop, t0, kv_end, a.scale_log2, m, lpart, acc, lane);
-      t0 += kDecodeTile;
-      if (t0 >= kv_end) break;
-      s_odd = tile_slot(rtt_row, t0 + 2 * kDecodeTile, kv_end, last, lane);
-      load_tile<D>(ta, s_even, kbase, vbase, row_elems, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile<D>(tb, qop, t0, kv_end, a.scale_log2, m, lpart, acc, lane);
-      t0 += kDecodeTile;
-      if (t0 >= kv_end) break;
-    }
-  }
-
+// Normalises one segment's accumulator and writes it: bf16 O and lse for a
+// request covered by one segment, else the fp32 partial and its log2-sum-exp.
+template <int D>
+__device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int part, float m, float lpart,
+                                               const floatx4 (&acc)[8], int h, bool head_ok, int j) {
+  h = opaque(h);
+  j = opaque(j);
   float l = lpart + __shfl_xor(lpart, 16);
   l += __shfl_xor(l, 32);
   const bool rows_ok = (D == 128) || (j < 2);
@@ -213,6 +170,104 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
   if (head_ok && j == 0) a.part_lse[(int64_t)part * a.hq + h] = lse2;
+}
+
+// One chunk (the request segments [s0, s1)) for one unit (kv head g,
+// 16-head group).  The chunk's tiles form one stream, so the software
+// pipeline runs across segment boundaries: while tile i is computed, the K/V
+// rows of tile i+1 are in flight and the slots of tile i+2 were requested
+// before them, whichever segments the three tiles belong to.  Two register
+// buffers are used in turn.  When the computed tile enters a new segment the
+// previous one is written out and the online-softmax state restarts.
+template <int D>
+__device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int s0, int s1, int unit, int4* win_rec,
+                                             int* win_row) {
+  const int g = unit / a.head_groups, hg = unit - g * a.head_groups;
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, j = lane >> 4;
+  const int hl = hg * 16 + l16;
+  const bool head_ok = hl < a.group;
+  const int h = g * a.group + hl;
+  const uint32_t row_elems = (uint32_t)a.hkv * D;
+  const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * D;
+  const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * D;
+  const uint32_t last = (uint32_t)(a.pool_slots - 1);
+
+  SegWindow w;
+  w.rec = win_rec;
+  w.row = win_row;
+  load_window(a, w, s0, s1, lane);
+  // first non-empty segment
+  TileCursor C = seg_at(a, w, s0, s1, lane);
+  C.t0 -= kDecodeTile;
+  C = next_tile<kDecodeTile>(a, w, C, s1, lane);
+  finish_empty<D>(a, w, s0, C.seg, s1, h, head_ok, j, lane);
+  if (C.seg >= s1) return;
+
+  u32x4 qop[D / 32];
+  load_q<D>(a, qop, C.b, h, head_ok, j);
+  float m = kNegInf, lpart = 0.f;
+  floatx4 acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto rtt_of = [&](const TileCursor& c) { return a.rtt + (int64_t)c.row * a.rtt_stride; };
+  KVTile<D> ta, tb;
+  load_tile<D>(ta, tile_slot(rtt_of(C), C.t0, C.kv_end, last, lane), kbase, vbase, row_elems, lane);
+  TileCursor L = next_tile<kDecodeTile>(a, w, C, s1, lane);
+  uint32_t s_odd = tile_slot(rtt_of(L), L.t0, L.kv_end, last, lane), s_even;
+  TileCursor S = next_tile<kDecodeTile>(a, w, L, s1, lane);
+
+  // after tile C is computed: shift the cursors and, on entering a new
+  // segment, write the finished one out and restart the softmax state
+  auto advance = [&]() -> bool {
+    const TileCursor prev = C;
+    C = L;
+    L = S;
+    S = next_tile<kDecodeTile>(a, w, S, s1, lane);
+    if (C.seg == prev.seg) return true;
+    finish_segment<D>(a, prev.b, prev.part, m, lpart, acc, h, head_ok, j);
+    finish_empty<D>(a, w, prev.seg + 1, C.seg, s1, h, head_ok, j, lane);
+    if (C.seg >= s1) return false;
+    load_q<D>(a, qop, C.b, h, head_ok, j);
+    m = kNegInf;
+    lpart = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    return true;
+  };
+
+  for (;;) {
+    s_even = tile_slot(rtt_of(S), S.t0, S.kv_end, last, lane);
+    load_tile<D>(tb, s_odd, kbase, vbase, row_elems, lane);
+    __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
+    compute_tile<D>(ta, qop, C.t0, C.kv_end, a.scale_log2, m, lpart, acc, lane);
+    if (!advance()) break;
+    s_odd = tile_slot(rtt_of(S), S.t0, S.kv_end, last, lane);
+    load_tile<D>(ta, s_even, kbase, vbase, row_elems, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile<D>(tb, qop, C.t0, C.kv_end, a.scale_log2, m, lpart, acc, lane);
+    if (!advance()) break;
+  }
+}
+
+// WPB waves per workgroup take WPB consecutive (kv head, head group) units of
+// the same chunk, so the rows of one token are requested together.  The plan
+// lays the requests' tiles end to end and cuts them into chunks of equal
+// length; a chunk is a list of request segments.
+template <int D, int WPB>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(DecodeArgs a) {
+  const int32_t* __restrict__ ws = a.ws;
+  const int c = (int)blockIdx.x;
+  if (c >= ws[WS_NCHUNKS]) return;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
+  const int unit = blockIdx.y * WPB + wv;
+  if (unit >= a.hkv * a.head_groups) return;
+  const int tab = ws[WS_CHUNK_TAB];
+  const int s0 = tab ? ws[tab + c] : c, s1 = tab ? ws[tab + c + 1] : c + 1;
+  __shared__ int4 win_rec[WPB][64];
+  __shared__ int win_row[WPB][64];
+  decode_chunk<D>(a, s0, s1, unit, win_rec[wv], win_row[wv]);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int32_t batch, hipStream_t s) {

@@ -19,6 +19,7 @@
 //  * Oᵀ += V8ᵀ·P8ᵀ: each lane gathers 16 keys x 8 channels of V8 and
 //    transposes the bytes with permutes into 8 A operands; 64 of the 128
 //    k slots carry the tile's keys, the rest are zero.
+#include "decode_stream.h"
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -36,7 +37,7 @@ __device__ __forceinline__ floatx4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, floatx4 
 struct Tile8 {
   u32x4 k[4][2];  // A operands of Sᵀ: 4 blocks of 16 keys, 32 bytes (channels 32j..32j+31)
   u32x2 v[16];    // the lane's 16 V rows, channels 8*(lane%16) .. +8
-  float ks[4];    // sfK of each 16-key block
+  float ks;       // sfK of 16-key block (lane & 3) of the tile
 };
 
 // token (within the tile) of element e (0..15) held by lane group j in the Pᵀ / Vᵀ operands
@@ -56,8 +57,7 @@ __device__ __forceinline__ void load_tile8(Tile8& t, uint32_t slot, int t0, int 
                                            uint32_t row_bytes, int lane) {
   // `slot`: slot of token (lane & 63) of the tile
   const int l16 = lane & 15, j = lane >> 4;
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) t.ks[blk] = sfk_row[min(t0 + 16 * blk, kv_end - 1) / k_block];
+  t.ks = sfk_row[min(t0 + 16 * (lane & 3), kv_end - 1) / k_block];
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
     const uint32_t sk = __shfl(slot, 16 * blk + l16);
@@ -92,126 +92,28 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 
 }  // namespace
 
-template <int WPB>
-__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_fp8_kernel(DecodeArgs a) {
+// Q8 of request b as the B operand (lane holds q8[h][32 j .. 32 j + 32]) and
+// the score factor sm_scale·log2(e)·sfQ[b,h].
+__device__ __forceinline__ void load_q8(const DecodeArgs& a, i32x8& qop, float& qscale, int b, int h, bool head_ok,
+                                        int j) {
   constexpr int D = 128;
-  const int32_t* __restrict__ ws = a.ws;
-  if ((int)blockIdx.x >= ws[WS_NUM_ITEMS]) return;
-  const int unit = blockIdx.y * WPB + (threadIdx.x >> 6);
-  if (unit >= a.hkv * a.head_groups) return;
-  const int4 it = reinterpret_cast<const int4*>(ws + a.items_off)[blockIdx.x];
-  const int b = it.x, kv_begin = it.y, kv_end = it.z, part = it.w;
-  const int g = unit / a.head_groups, hg = unit - g * a.head_groups;
-  const int lane = threadIdx.x & 63;
-  const int l16 = lane & 15, j = lane >> 4;
-  const int hl = hg * 16 + l16;
-  const bool head_ok = hl < a.group;
-  const int h = g * a.group + (head_ok ? hl : 0);
-  const int row = a.rpi ? a.rpi[b] : b;
-  const int32_t* __restrict__ rtt_row = a.rtt + (int64_t)row * a.rtt_stride;
-  const uint32_t row_bytes = (uint32_t)a.hkv * D;
-  const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k_pool) + (int64_t)g * D;
-  const uint8_t* __restrict__ vbase = static_cast<const uint8_t*>(a.v_pool) + (int64_t)g * D;
-  const float* __restrict__ sfk_row = a.sfk + ((int64_t)b * a.hkv + g) * a.sfk_stride;
+  h = opaque(h);
+  j = opaque(j);
+  const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + ((int64_t)b * a.hq + h) * D + 32 * j;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  const u32x4 q0 = head_ok ? ldg16(qrow) : z, q1 = head_ok ? ldg16(qrow + 16) : z;
+  qop = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3], (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
+  qscale = head_ok ? a.sfq[(int64_t)b * a.hq + h] * a.scale_log2 : 0.f;
+}
 
-  // Q8 as the B operand: lane holds q8[h][32 j .. 32 j + 32]
-  i32x8 qop;
-  {
-    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + ((int64_t)b * a.hq + h) * D + 32 * j;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 q0 = head_ok ? ldg16(qrow) : z, q1 = head_ok ? ldg16(qrow + 16) : z;
-    qop = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3], (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
-  }
-  const float qscale = head_ok ? a.sfq[(int64_t)b * a.hq + h] * a.scale_log2 : 0.f;
-
-  float m = kNegInf, lpart = 0.f;
-  floatx4 acc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const Tile8& cur, int t0) {
-    // ---- scores: 4 blocks of 16 keys; every 16-key block lies in one sfK block
-    float sc[16];
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const i32x8 kop = {(int)cur.k[blk][0][0], (int)cur.k[blk][0][1], (int)cur.k[blk][0][2], (int)cur.k[blk][0][3],
-                         (int)cur.k[blk][1][0], (int)cur.k[blk][1][1], (int)cur.k[blk][1][2], (int)cur.k[blk][1][3]};
-      floatx4 s = {0.f, 0.f, 0.f, 0.f};
-      s = mfma_fp8_16x16x128(kop, qop, s);
-      const int tb = t0 + 16 * blk;
-      const float ks = cur.ks[blk] * qscale;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[4 * blk + r] = (tb + 4 * j + r < kv_end) ? s[r] * ks : kNegInf;
-    }
-    float mx = sc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);  // finite: key t0 is in range
-    const float alpha = exp2_fast(m - m_new);
-    m = m_new;
-    float p[16];
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = exp2_fast(sc[e] - m_new);
-      ps += p[e];
-    }
-    lpart = lpart * alpha + ps;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] *= alpha;
-    // P8ᵀ operand: element e (byte e) <-> key tok_of(j, e); bytes 16..31 are zero
-    i32x8 pop;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      pop[w] = (int)pack_fp8x4(448.f * p[4 * w], 448.f * p[4 * w + 1], 448.f * p[4 * w + 2], 448.f * p[4 * w + 3]);
-    pop[4] = pop[5] = pop[6] = pop[7] = 0;
-    // V8ᵀ operands: block c holds channel 8*l16 + c of the lane's 16 keys
-    uint32_t vt[8][4];  // [channel c][key group of 4]
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      uint32_t o_lo[4], o_hi[4];
-      transpose4x4(cur.v[4 * q4][0], cur.v[4 * q4 + 1][0], cur.v[4 * q4 + 2][0], cur.v[4 * q4 + 3][0], o_lo);
-      transpose4x4(cur.v[4 * q4][1], cur.v[4 * q4 + 1][1], cur.v[4 * q4 + 2][1], cur.v[4 * q4 + 3][1], o_hi);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        vt[c][q4] = o_lo[c];
-        vt[4 + c][q4] = o_hi[c];
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const i32x8 vop = {(int)vt[c][0], (int)vt[c][1], (int)vt[c][2], (int)vt[c][3], 0, 0, 0, 0};
-      acc[c] = mfma_fp8_16x16x128(vop, pop, acc[c]);
-    }
-  };
-
-  if (kv_begin < kv_end) {
-    // Two register buffers in turn (as in the bf16 decode): while tile i is
-    // computed the rows of tile i+1 are in flight, and the slots of tile i+2
-    // were requested before them.
-    const uint32_t last = (uint32_t)(a.pool_slots - 1);
-    Tile8 ta, tb;
-    uint32_t s_odd, s_even = slot_at(rtt_row, kv_begin, kv_end, last, lane);
-    load_tile8(ta, s_even, kv_begin, kv_end, sfk_row, a.k_block, kbase, vbase, row_bytes, lane);
-    s_odd = slot_at(rtt_row, kv_begin + kTile8, kv_end, last, lane);
-    for (int t0 = kv_begin;;) {
-      s_even = slot_at(rtt_row, t0 + 2 * kTile8, kv_end, last, lane);
-      load_tile8(tb, s_odd, t0 + kTile8, kv_end, sfk_row, a.k_block, kbase, vbase, row_bytes, lane);
-      __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
-      compute(ta, t0);
-      t0 += kTile8;
-      if (t0 >= kv_end) break;
-      s_odd = slot_at(rtt_row, t0 + 2 * kTile8, kv_end, last, lane);
-      load_tile8(ta, s_even, t0 + kTile8, kv_end, sfk_row, a.k_block, kbase, vbase, row_bytes, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(tb, t0);
-      t0 += kTile8;
-      if (t0 >= kv_end) break;
-    }
-  }
-
+// Applies the per-channel V scale (and mean) to one segment's accumulator and
+// writes it: bf16 O and lse for a request covered by one segment, else the
+// fp32 partial and its log2-sum-exp.
+__device__ __forceinline__ void finish_segment8(const DecodeArgs& a, int b, int g, int part, float m, float lpart,
+                                                const floatx4 (&acc)[8], int h, bool head_ok, int j) {
+  constexpr int D = 128;
+  h = opaque(h);
+  j = opaque(j);
   float l = lpart + __shfl_xor(lpart, 16);
   l += __shfl_xor(l, 32);
   // Oᵀ block c, row 4 j + r  <->  channel d = 8 (4 j + r) + c = 32 j + 8 r + c
@@ -250,6 +152,160 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     if (j == 0) a.part_lse[(int64_t)part * a.hq + h] = lse2;
   }
+}
+
+// One chunk (the request segments [s0, s1)) for one unit (kv head g,
+// 16-head group), its 64-token tiles walked as one stream as in the bf16
+// decode: while tile i is computed the rows of tile i+1 are in flight and
+// the slots of tile i+2 were requested before them, whichever segments the
+// tiles belong to.
+__device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, int s1, int unit, int4* win_rec,
+                                                 int* win_row) {
+  constexpr int D = 128;
+  const int g = unit / a.head_groups, hg = unit - g * a.head_groups;
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, j = lane >> 4;
+  const int hl = hg * 16 + l16;
+  const bool head_ok = hl < a.group;
+  const int h = g * a.group + (head_ok ? hl : 0);
+  const uint32_t row_bytes = (uint32_t)a.hkv * D;
+  const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k_pool) + (int64_t)g * D;
+  const uint8_t* __restrict__ vbase = static_cast<const uint8_t*>(a.v_pool) + (int64_t)g * D;
+  const uint32_t last = (uint32_t)(a.pool_slots - 1);
+
+  SegWindow w;
+  w.rec = win_rec;
+  w.row = win_row;
+  load_window(a, w, s0, s1, lane);
+  // first non-empty segment
+  TileCursor C = seg_at(a, w, s0, s1, lane);
+  C.t0 -= kTile8;
+  C = next_tile<kTile8>(a, w, C, s1, lane);
+  finish_empty<D>(a, w, s0, C.seg, s1, h, head_ok, j, lane);
+  if (C.seg >= s1) return;
+
+  i32x8 qop;
+  float qscale;
+  load_q8(a, qop, qscale, C.b, h, head_ok, j);
+  float m = kNegInf, lpart = 0.f;
+  floatx4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Tile8& cur, int t0, int kv_end) {
+    // ---- scores: 4 blocks of 16 keys; every 16-key block lies in one sfK block
+    float sc[16];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const i32x8 kop = {(int)cur.k[blk][0][0], (int)cur.k[blk][0][1], (int)cur.k[blk][0][2], (int)cur.k[blk][0][3],
+                         (int)cur.k[blk][1][0], (int)cur.k[blk][1][1], (int)cur.k[blk][1][2], (int)cur.k[blk][1][3]};
+      floatx4 s = {0.f, 0.f, 0.f, 0.f};
+      s = mfma_fp8_16x16x128(kop, qop, s);
+      const int tb = t0 + 16 * blk;
+      const float ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cur.ks), blk)) * qscale;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[4 * blk + r] = (tb + 4 * j + r < kv_end) ? s[r] * ks : kNegInf;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);  // finite: key t0 is in range
+    const float alpha = exp2_fast(m - m_new);
+    m = m_new;
+    float p[16];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = exp2_fast(sc[e] - m_new);
+      ps += p[e];
+    }
+    lpart = lpart * alpha + ps;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+    // P8ᵀ operand: element e (byte e) <-> key tok_of(j, e); bytes 16..31 are zero
+    i32x8 pop;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      pop[q] = (int)pack_fp8x4(448.f * p[4 * q], 448.f * p[4 * q + 1], 448.f * p[4 * q + 2], 448.f * p[4 * q + 3]);
+    pop[4] = pop[5] = pop[6] = pop[7] = 0;
+    // V8ᵀ operands: block c holds channel 8*l16 + c of the lane's 16 keys
+    uint32_t vt[8][4];  // [channel c][key group of 4]
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      uint32_t o_lo[4], o_hi[4];
+      transpose4x4(cur.v[4 * q4][0], cur.v[4 * q4 + 1][0], cur.v[4 * q4 + 2][0], cur.v[4 * q4 + 3][0], o_lo);
+      transpose4x4(cur.v[4 * q4][1], cur.v[4 * q4 + 1][1], cur.v[4 * q4 + 2][1], cur.v[4 * q4 + 3][1], o_hi);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        vt[c][q4] = o_lo[c];
+        vt[4 + c][q4] = o_hi[c];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const i32x8 vop = {(int)vt[c][0], (int)vt[c][1], (int)vt[c][2], (int)vt[c][3], 0, 0, 0, 0};
+      acc[c] = mfma_fp8_16x16x128(vop, pop, acc[c]);
+    }
+  };
+
+  auto rtt_of = [&](const TileCursor& c) { return a.rtt + (int64_t)c.row * a.rtt_stride; };
+  auto sfk_of = [&](const TileCursor& c) { return a.sfk + ((int64_t)c.b * a.hkv + g) * a.sfk_stride; };
+  Tile8 ta, tb;
+  load_tile8(ta, slot_at(rtt_of(C), C.t0, C.kv_end, last, lane), C.t0, C.kv_end, sfk_of(C), a.k_block, kbase, vbase,
+             row_bytes, lane);
+  TileCursor L = next_tile<kTile8>(a, w, C, s1, lane);
+  uint32_t s_odd = slot_at(rtt_of(L), L.t0, L.kv_end, last, lane), s_even;
+  TileCursor S = next_tile<kTile8>(a, w, L, s1, lane);
+
+  // after tile C is computed: shift the cursors and, on entering a new
+  // segment, write the finished one out and restart the softmax state
+  auto advance = [&]() -> bool {
+    const TileCursor prev = C;
+    C = L;
+    L = S;
+    S = next_tile<kTile8>(a, w, S, s1, lane);
+    if (C.seg == prev.seg) return true;
+    finish_segment8(a, prev.b, g, prev.part, m, lpart, acc, h, head_ok, j);
+    finish_empty<D>(a, w, prev.seg + 1, C.seg, s1, h, head_ok, j, lane);
+    if (C.seg >= s1) return false;
+    load_q8(a, qop, qscale, C.b, h, head_ok, j);
+    m = kNegInf;
+    lpart = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    return true;
+  };
+
+  for (;;) {
+    s_even = slot_at(rtt_of(S), S.t0, S.kv_end, last, lane);
+    load_tile8(tb, s_odd, L.t0, L.kv_end, sfk_of(L), a.k_block, kbase, vbase, row_bytes, lane);
+    __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
+    compute(ta, C.t0, C.kv_end);
+    if (!advance()) break;
+    s_odd = slot_at(rtt_of(S), S.t0, S.kv_end, last, lane);
+    load_tile8(ta, s_even, L.t0, L.kv_end, sfk_of(L), a.k_block, kbase, vbase, row_bytes, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(tb, C.t0, C.kv_end);
+    if (!advance()) break;
+  }
+}
+
+// WPB units of one chunk per workgroup, as in the bf16 decode.
+template <int WPB>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_fp8_kernel(DecodeArgs a) {
+  const int32_t* __restrict__ ws = a.ws;
+  const int c = (int)blockIdx.x;
+  if (c >= ws[WS_NCHUNKS]) return;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
+  const int unit = blockIdx.y * WPB + wv;
+  if (unit >= a.hkv * a.head_groups) return;
+  const int tab = ws[WS_CHUNK_TAB];
+  const int s0 = tab ? ws[tab + c] : c, s1 = tab ? ws[tab + c + 1] : c + 1;
+  __shared__ int4 win_rec[WPB][64];
+  __shared__ int win_row[WPB][64];
+  decode_fp8_chunk(a, s0, s1, unit, win_rec[wv], win_row[wv]);
 }
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch, hipStream_t s) {

@@ -20,6 +20,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
+// Returns x unchanged but opaque to the optimiser, so the addresses derived
+// from it in rarely run code (a segment's epilogue inside the tile loop) are
+// computed there, not hoisted out of the loop into registers it needs.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ldg8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

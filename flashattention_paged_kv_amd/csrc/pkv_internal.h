@@ -27,6 +27,8 @@ enum : int {
   WS_CAPACITY = 3,
   WS_CHUNK = 4,  // decode: chunk tiles; extend: block tokens
   WS_TARGET = 5, // decode: the item count the chunk was sized for
+  WS_NCHUNKS = 6,    // decode: chunks (workgroups) of request segments
+  WS_CHUNK_TAB = 7,  // decode: word offset of the chunk -> first segment table [NCHUNKS+1], 0 = one segment each
   WS_HEADER_INTS = 16
 };
 
@@ -69,8 +71,10 @@ inline int64_t decode_capacity(const pkv_params& p, int64_t batch, int64_t targe
     int64_t per = ceil_div(p.max_kv_len, p.kv_chunk);
     return batch * (per > 0 ? per : 1);
   }
-  // the chunk search never gives more than max(target, batch) items
-  const int64_t a = target_items > batch ? target_items : batch, b = batch * max_tiles;
+  // balanced chunks: at most target_items chunks, and every chunk boundary
+  // inside a request adds one segment; a request never has more segments
+  // than tiles
+  const int64_t a = target_items + batch, b = batch * max_tiles;
   return a < b ? a : b;
 }
 

@@ -6,12 +6,13 @@
 // One workgroup of 1024 threads: block reductions / scans over the requests,
 // then an item table written in parallel.
 //
-// Decode: the automatic chunk is the smallest number of 32-token tiles for
-// which the batch splits into at most target_items items (the items whose
-// waves the device holds at once), found by bisection over the chunk size;
-// the launch then runs in one pass.  Items stay in request order unless they
-// exceed that count (many short requests, or a fixed kv_chunk), in which case
-// they are ordered longest first so the short ones fill the tail.
+// Decode, automatic: the requests' 32-token tiles, laid end to end, are cut
+// into at most target_items equal chunks (target_items = the items whose
+// waves the device holds at once), so the launch runs in one pass and every
+// workgroup streams the same amount of KV.  A chunk is a short list of
+// request segments; a request cut by chunk boundaries writes split partials
+// that the merge combines.  Decode with a fixed kv_chunk: one item per split,
+// ordered longest first when there are more than target_items.
 // Extend: items are ordered by causal KV range, longest first.
 // Ordering is a bitonic sort on (length, index) keys, in LDS up to
 // kPlanLdsSortMax items and in the workspace's key area beyond that.
@@ -54,26 +55,6 @@ __device__ int64_t block_exclusive_scan(int64_t v, int64_t* sh /*[16]*/, int64_t
   *total = sh[16];
   __syncthreads();
   return ex;
-}
-
-__device__ int64_t block_max(int64_t v, int64_t* sh /*[17]*/) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    int64_t u = __shfl_xor(v, off, 64);
-    v = u > v ? u : v;
-  }
-  if (lane == 0) sh[wave] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t m = sh[0];
-    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = sh[w] > m ? sh[w] : m;
-    sh[16] = m;
-  }
-  __syncthreads();
-  const int64_t r = sh[16];
-  __syncthreads();
-  return r;
 }
 
 __device__ __forceinline__ int clamp_len(int L, int max_kv_len) {
@@ -125,50 +106,100 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int B = a.batch;
   int64_t carry = 0;
 
-  if (a.mode == PKV_DECODE) {
-    // 1. total and largest tile counts
-    int64_t my_tiles = 0, my_max = 0;
-    for (int b = threadIdx.x; b < B; b += blockDim.x) {
-      const int64_t t = (clamp_len(a.seq_lens[b], a.max_kv_len) + kDecodeTile - 1) / kDecodeTile;
-      my_tiles += t;
-      my_max = t > my_max ? t : my_max;
+  if (a.mode == PKV_DECODE && a.kv_chunk == 0) {
+    // Balanced chunks: the requests' 32-token tiles laid end to end (request
+    // b at global tiles [o_b, o_b + t_b)) are cut into chunks of C tiles,
+    // C = ceil(T / target); a chunk is one workgroup and holds the request
+    // segments it overlaps, so every workgroup streams the same amount of KV.
+    int32_t* goff = ws + a.tmp_off;  // [B+1] global tile offset of each request
+    for (int base = 0; base < B; base += blockDim.x) {
+      const int b = base + threadIdx.x;
+      const int64_t t = b < B ? (clamp_len(a.seq_lens[b], a.max_kv_len) + kDecodeTile - 1) / kDecodeTile : 0;
+      int64_t tot;
+      const int64_t ex = block_exclusive_scan(t, sh, &tot);
+      if (b < B) goff[b] = (int32_t)(carry + ex);
+      carry += tot;
     }
-    int64_t total_tiles;
-    (void)block_exclusive_scan(my_tiles, sh, &total_tiles);
-    const int64_t max_tiles = block_max(my_max, sh);
-    // items the batch splits into for a chunk of c tiles (a request has >= 1)
-    auto count_items = [&](int64_t c) {
-      int64_t mine = 0;
-      for (int b = threadIdx.x; b < B; b += blockDim.x) {
-        const int64_t t = (clamp_len(a.seq_lens[b], a.max_kv_len) + kDecodeTile - 1) / kDecodeTile;
-        const int64_t n = (t + c - 1) / c;
-        mine += n < 1 ? 1 : n;
+    const int64_t T = carry;
+    if (threadIdx.x == 0) goff[B] = (int32_t)T;
+    int64_t C = (T + a.target_items - 1) / a.target_items;
+    C = C < 1 ? 1 : C;
+    int64_t nchunks = (T + C - 1) / C;
+    nchunks = nchunks < 1 ? 1 : nchunks;
+    __threadfence_block();
+    __syncthreads();
+    // segments per request (an empty request keeps one empty segment)
+    carry = 0;
+    for (int base = 0; base < B; base += blockDim.x) {
+      const int b = base + threadIdx.x;
+      int64_t nseg = 0;
+      if (b < B) {
+        const int64_t o = goff[b], t = goff[b + 1] - o;
+        nseg = t == 0 ? 1 : (o + t - 1) / C - o / C + 1;
       }
       int64_t tot;
-      (void)block_exclusive_scan(mine, sh, &tot);
-      return tot;
-    };
-    int64_t chunk;
-    if (a.kv_chunk > 0) {
-      chunk = a.kv_chunk / kDecodeTile;
-    } else {
-      // smallest chunk with count_items(chunk) <= target (count is non-increasing
-      // in the chunk; at max_tiles every request is one item)
-      const int64_t T = a.target_items;
-      int64_t hi = max_tiles > 0 ? max_tiles : 1;
-      int64_t lo = (total_tiles + T - 1) / T;
-      lo = lo < 1 ? 1 : (lo > hi ? hi : lo);
-      if (count_items(hi) > T) {
-        chunk = hi;
-      } else {
-        while (lo < hi) {  // block-uniform: every bound comes from a block total
-          const int64_t mid = (lo + hi) >> 1;
-          if (count_items(mid) <= T) hi = mid; else lo = mid + 1;
+      const int64_t ex = block_exclusive_scan(nseg, sh, &tot);
+      if (b < B) req[b] = (int32_t)(carry + ex);
+      carry += tot;
+    }
+    if (threadIdx.x == 0) req[B] = (int32_t)carry;
+    const int64_t num = carry < a.capacity ? carry : a.capacity;
+    __threadfence_block();
+    __syncthreads();
+    // segments (b, kv_begin, kv_end, partial index) in request order, and
+    // the chunk of each (non-decreasing along the list)
+    int32_t* seg_chunk = ws + a.keys_off;
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+      const int L = clamp_len(a.seq_lens[b], a.max_kv_len);
+      const int64_t o = goff[b], t = goff[b + 1] - o;
+      const int first = req[b], n = req[b + 1] - req[b];
+      if (t == 0) {
+        if (first < num) {
+          items[first] = make_int4(b, 0, 0, -1);
+          const int64_t cc = o / C;
+          seg_chunk[first] = (int32_t)(cc < nchunks ? cc : nchunks - 1);
         }
-        chunk = lo;
+        continue;
+      }
+      for (int sgi = 0; sgi < n && first + sgi < num; ++sgi) {
+        const int64_t cc = o / C + sgi;
+        const int64_t g0 = o > cc * C ? o : cc * C;
+        const int64_t g1 = o + t < (cc + 1) * C ? o + t : (cc + 1) * C;
+        const int kb = (int)((g0 - o) * kDecodeTile);
+        const int ke = (int)((g1 - o) * kDecodeTile < L ? (g1 - o) * kDecodeTile : L);
+        items[first + sgi] = make_int4(b, kb, ke, n > 1 ? first + sgi : -1);
+        seg_chunk[first + sgi] = (int32_t)cc;
       }
     }
-    // 2. splits per request, exclusive scan -> req[]
+    __threadfence_block();
+    __syncthreads();
+    // chunk table: first segment of each chunk
+    int32_t* tab = ws + a.tmp_off + B + 1;
+    for (int64_t cc = threadIdx.x; cc <= nchunks; cc += blockDim.x) {
+      int lo = 0, hi = (int)num;  // first segment with chunk >= cc
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (seg_chunk[mid] < cc) lo = mid + 1; else hi = mid;
+      }
+      tab[cc] = cc == nchunks ? (int32_t)num : lo;
+    }
+    if (threadIdx.x == 0) {
+      ws[WS_MODE] = PKV_DECODE;
+      ws[WS_BATCH] = B;
+      ws[WS_NUM_ITEMS] = (int32_t)num;
+      ws[WS_CAPACITY] = (int32_t)a.capacity;
+      ws[WS_CHUNK] = (int32_t)C;
+      ws[WS_TARGET] = a.target_items;
+      ws[WS_NCHUNKS] = (int32_t)nchunks;
+      ws[WS_CHUNK_TAB] = (int32_t)(a.tmp_off + B + 1);
+    }
+    return;
+  }
+
+  if (a.mode == PKV_DECODE) {
+    // Fixed splits of kv_chunk tokens per request; each split is its own
+    // chunk.  Ordered longest first when they overflow the target.
+    const int64_t chunk = a.kv_chunk / kDecodeTile;
     for (int base = 0; base < B; base += blockDim.x) {
       int b = base + threadIdx.x;
       int64_t splits = 0;
@@ -186,9 +217,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int64_t num = carry < a.capacity ? carry : a.capacity;
     __threadfence_block();
     __syncthreads();
-    // 3. items (b, kv_begin, kv_end, partial index), created request-major;
-    //    the partial index of split s of request b is req[b] + s.  Sorted
-    //    (through tmp) only when they overflow the target.
+    // items (b, kv_begin, kv_end, partial index), created request-major; the
+    // partial index of split s of request b is req[b] + s
     const bool sorted = num > a.target_items;
     int4* tmp = reinterpret_cast<int4*>(ws + (sorted ? a.tmp_off : a.items_off));
     const int n2 = sorted ? sort_size(num) : (int)num;
@@ -229,6 +259,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       ws[WS_CAPACITY] = (int32_t)a.capacity;
       ws[WS_CHUNK] = (int32_t)chunk;
       ws[WS_TARGET] = a.target_items;
+      ws[WS_NCHUNKS] = (int32_t)num;
+      ws[WS_CHUNK_TAB] = 0;
     }
     return;
   }

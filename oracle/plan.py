@@ -11,27 +11,33 @@ for bit.  Its pins are invariants, not values from the pages.
 Decode rule (tile = 32 tokens):
 
 * L_b is clamped to [0, max_kv_len]; tiles_b = ceil(L_b / 32).
-* units = Hkv · ceil(G / 16) work items per split (one per kv head and
-  16-row head group).  ``target_items`` is the number of split items the
-  chunk is sized for: ceil(split_target / units) when the caller gives a
-  split_target, otherwise the number of items whose waves the device holds
-  at once (the library queries the decode kernel's occupancy; it is an
-  input here and the GPU plan records it in its header).
-* automatic chunk: the smallest c >= 1 with Σ_b max(1, ceil(tiles_b / c))
-  <= target_items; if even c = max_b tiles_b gives more (every request is
-  then one item), c = max(1, max_b tiles_b).
-  fixed chunk (``kv_chunk`` tokens, a multiple of 32): c = kv_chunk / 32.
-* splits_b = max(1, ceil(tiles_b / c)); split s covers tiles
+* units = Hkv · ceil(G / 16) waves per item (one per kv head and 16-row head
+  group).  ``target_items`` is the number of chunks the work is cut into at
+  most: ceil(split_target / units) when the caller gives a split_target,
+  otherwise the number of items whose waves the device holds at once (the
+  library queries the decode kernel's occupancy; it is an input here and the
+  GPU plan records it in its header).
+* automatic (kv_chunk = 0), balanced chunks: request b occupies global tiles
+  [o_b, o_b + tiles_b) with o the exclusive prefix sum of tiles, T = Σ tiles_b.
+  Chunk size C = max(1, ceil(T / target_items)); nchunks = max(1, ceil(T / C)).
+  Chunk c covers global tiles [c·C, (c+1)·C).  Request b is cut into the
+  segments it shares with the chunks it overlaps: segment s lies in chunk
+  ⌊o_b / C⌋ + s and covers tokens [32·(g0 - o_b), min(32·(g1 - o_b), L_b)),
+  g0/g1 the overlap's global tile bounds.  An empty request is one empty
+  segment in chunk min(⌊o_b / C⌋, nchunks - 1).  Segments are listed request
+  by request (so chunks are non-decreasing along the list) and chunk c owns
+  the segments [tab[c], tab[c+1]).
+* fixed chunk (``kv_chunk`` tokens, a multiple of 32): c = kv_chunk / 32,
+  splits_b = max(1, ceil(tiles_b / c)); split s covers tiles
   [⌊s·tiles_b/splits_b⌋, ⌊(s+1)·tiles_b/splits_b⌋), i.e. tokens
-  [32·t0, min(32·t1, L_b)) (balanced, interior bounds on tile multiples).
-* items are created request-major (b, s); a request with one split writes
-  its output directly (part index -1), otherwise split s of request b owns
-  partial slot split_off[b] + s with split_off the exclusive prefix sum.
-  When there are more items than target_items the list is ordered by split
-  length (tokens) descending, ties by creation order (longest first, so the
-  short splits fill the tail); otherwise it stays in creation order.
+  [32·t0, min(32·t1, L_b)).  Each split is its own chunk; when there are more
+  splits than target_items they are ordered by length (tokens) descending,
+  ties by creation order, otherwise they stay in request order.
+* a request with one segment writes its output directly (part index -1);
+  otherwise segment s of request b owns partial slot split_off[b] + s, with
+  split_off the exclusive prefix sum of segments per request.
 * capacity (host-visible, never exceeded):
-  automatic: min(max(target_items, B), B · max(1, ceil(max_kv_len / 32)));
+  automatic: min(target_items + B, B · max(1, ceil(max_kv_len / 32)));
   fixed: B · max(1, ceil(max_kv_len / kv_chunk)).
 
 Extend rule: rows of a work item are (head, token) pairs of one kv head,
@@ -63,43 +69,63 @@ def decode_capacity(batch: int, max_kv_len: int, target_items: int, kv_chunk: in
     if kv_chunk > 0:
         return batch * max(1, _ceil_div(max_kv_len, kv_chunk))
     max_tiles = max(1, _ceil_div(max_kv_len, DECODE_TILE))
-    return min(max(target_items, batch), batch * max_tiles)
+    return min(target_items + batch, batch * max_tiles)
 
 
 def plan_decode(seq_lens, max_kv_len: int, target_items: int, kv_chunk: int = 0) -> Dict:
-    L = np.clip(np.asarray(seq_lens, dtype=np.int64), 0, max_kv_len)
+    L = [int(x) for x in np.clip(np.asarray(seq_lens, dtype=np.int64), 0, max_kv_len)]
     B = len(L)
-    tiles = [_ceil_div(int(x), DECODE_TILE) for x in L]
-
-    def count_items(c):
-        return sum(max(1, _ceil_div(t, c)) for t in tiles)
-
+    tiles = [_ceil_div(x, DECODE_TILE) for x in L]
+    items, seg_chunk = [], []
+    splits = []
     if kv_chunk > 0:
         assert kv_chunk % DECODE_TILE == 0
         chunk = kv_chunk // DECODE_TILE
+        for b in range(B):
+            n = max(1, _ceil_div(tiles[b], chunk))
+            splits.append(n)
+            for s in range(n):
+                t0 = (s * tiles[b]) // n
+                t1 = ((s + 1) * tiles[b]) // n
+                items.append([b, t0 * DECODE_TILE, min(t1 * DECODE_TILE, L[b]), s])
+        if len(items) > target_items:
+            order = sorted(range(len(items)), key=lambda i: (-(items[i][2] - items[i][1]), i))
+            items = [items[i] for i in order]
+        nchunks = len(items)
+        chunk_tab = list(range(nchunks + 1))
     else:
-        top = max([1] + tiles)
-        chunk = next((c for c in range(1, top + 1) if count_items(c) <= target_items), top)
-    splits = [max(1, _ceil_div(t, chunk)) for t in tiles]
+        T = sum(tiles)
+        chunk = max(1, _ceil_div(T, target_items))
+        nchunks = max(1, _ceil_div(T, chunk))
+        o = 0
+        for b in range(B):
+            if tiles[b] == 0:
+                splits.append(1)
+                items.append([b, 0, 0, 0])
+                seg_chunk.append(min(o // chunk, nchunks - 1))
+                continue
+            first_c, last_c = o // chunk, (o + tiles[b] - 1) // chunk
+            splits.append(last_c - first_c + 1)
+            for s, c in enumerate(range(first_c, last_c + 1)):
+                g0 = max(o, c * chunk)
+                g1 = min(o + tiles[b], (c + 1) * chunk)
+                items.append([b, (g0 - o) * DECODE_TILE, min((g1 - o) * DECODE_TILE, L[b]), s])
+                seg_chunk.append(c)
+            o += tiles[b]
+        chunk_tab = [next((i for i, c in enumerate(seg_chunk) if c >= cc), len(items))
+                     for cc in range(nchunks)] + [len(items)]
     split_off = [0]
-    for s in splits:
-        split_off.append(split_off[-1] + s)
-    items = []
-    for b in range(B):
-        for s in range(splits[b]):
-            t0 = (s * tiles[b]) // splits[b]
-            t1 = ((s + 1) * tiles[b]) // splits[b]
-            kb = t0 * DECODE_TILE
-            ke = min(t1 * DECODE_TILE, int(L[b]))
-            part = split_off[b] + s if splits[b] > 1 else -1
-            items.append((b, kb, ke, part))
-    if len(items) > target_items:
-        order = sorted(range(len(items)), key=lambda i: (-(items[i][2] - items[i][1]), i))
-        items = [items[i] for i in order]
+    for n in splits:
+        split_off.append(split_off[-1] + n)
+    for it in items:  # segment index -> partial slot, or -1 for a whole request
+        b, s = it[0], it[3]
+        it[3] = split_off[b] + s if splits[b] > 1 else -1
     cap = decode_capacity(B, max_kv_len, target_items, kv_chunk)
+    assert len(items) <= cap
     return {"chunk_tiles": chunk, "splits": np.array(splits, np.int64),
             "split_off": np.array(split_off, np.int64), "target_items": target_items,
-            "items": np.array(items, np.int64).reshape(-1, 4), "capacity": cap}
+            "items": np.array(items, np.int64).reshape(-1, 4), "capacity": cap,
+            "nchunks": nchunks, "chunk_tab": np.array(chunk_tab, np.int64)}
 
 
 def extend_block_tokens(group: int) -> int:

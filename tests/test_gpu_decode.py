@@ -188,6 +188,11 @@ def test_plan_matches_oracle_rederivation_bit_for_bit():
         assert n == len(ref["items"]) and ws[3] == ref["capacity"] and ws[4] == ref["chunk_tiles"]
         assert np.array_equal(items, ref["items"])
         assert np.array_equal(ws[16:16 + B + 1], ref["split_off"])
+        assert ws[6] == ref["nchunks"]
+        if kv_chunk:
+            assert ws[7] == 0  # identity: one split per chunk
+        else:
+            assert np.array_equal(ws[ws[7]:ws[7] + ws[6] + 1], ref["chunk_tab"])
 
 
 def test_kv_store_round_trip_bit_exact():

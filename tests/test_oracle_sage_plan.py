@@ -112,18 +112,32 @@ def test_decode_plan_invariants(seed, kv_chunk):
     tiles = -(-Lc // oracle.DECODE_TILE)
     parts = []
     lengths = items[:, 2] - items[:, 1]
-    if len(items) > target:
+    tab = plan["chunk_tab"]
+    assert tab[0] == 0 and tab[-1] == len(items) and np.all(np.diff(tab) >= 1)
+    assert len(tab) == plan["nchunks"] + 1
+    if kv_chunk and len(items) > target:
         assert np.all(np.diff(lengths) <= 0)  # longest split first
     else:
         assert list(items[:, 0]) == sorted(items[:, 0])  # request order
     if not kv_chunk:
-        count = lambda c: int(np.maximum(1, -(-tiles // c)).sum())
-        c = plan["chunk_tiles"]
-        assert len(items) == count(c)
-        # the chunk is the smallest meeting the target (or one item per request)
-        assert count(c) <= max(target, B)
+        # balanced chunks: every chunk but the last holds exactly C tiles, the
+        # last at most C; C is the smallest size giving <= target chunks
+        c, T = plan["chunk_tiles"], int(tiles.sum())
+        seg_tiles = -(-lengths // oracle.DECODE_TILE)
+        per_chunk = [int(seg_tiles[tab[k]:tab[k + 1]].sum()) for k in range(plan["nchunks"])]
+        assert sum(per_chunk) == T
+        if T:
+            assert all(x == c for x in per_chunk[:-1]) and 1 <= per_chunk[-1] <= c
+        assert plan["nchunks"] <= target
         if c > 1:
-            assert count(c - 1) > target
+            assert -(-T // (c - 1)) > target
+        # a request crosses chunks only at chunk boundaries (global tile offsets)
+        starts = np.concatenate([[0], np.cumsum(tiles)])
+        for k in range(plan["nchunks"]):
+            for i in range(tab[k], tab[k + 1]):
+                g0 = starts[items[i, 0]] + items[i, 1] // oracle.DECODE_TILE
+                if seg_tiles[i]:
+                    assert k * c <= g0 and g0 + seg_tiles[i] <= (k + 1) * c
     for b in range(B):
         mine = items[items[:, 0] == b]
         mine = mine[np.argsort(mine[:, 1], kind="stable")]
