@@ -170,6 +170,7 @@ int pkv_plan_metadata(const pkv_params* params, int32_t mode, int32_t batch, int
   if (tgt > INT32_MAX) return fail(PKV_EUNSUPPORTED, "split target %lld exceeds int32", (long long)tgt);
   a.target_items = (int32_t)tgt;
   a.block_tokens = pkv::extend_block_tokens(*params);
+  a.tile = pkv::decode_plan_tile(*params);
   return check_launch(pkv::launch_plan(a, static_cast<hipStream_t>(stream)), "plan_metadata launch");
 }
 

@@ -65,8 +65,14 @@ inline int64_t decode_target_items(const pkv_params& p, int64_t resident_items) 
   return t > 1 ? t : 1;
 }
 
+// Granularity of the automatic decode chunks: the decode kernel's tile (32
+// tokens for bf16 K/V, 64 for 8-bit), so segment bounds inside a request fall
+// on tile bounds and no tile is cut short except at a request's end.
+inline int decode_plan_tile(const pkv_params& p) { return p.kv_dtype == PKV_FP8_E4M3 ? 64 : kDecodeTile; }
+
 inline int64_t decode_capacity(const pkv_params& p, int64_t batch, int64_t target_items) {
-  const int64_t max_tiles = ceil_div(p.max_kv_len, kDecodeTile) > 0 ? ceil_div(p.max_kv_len, kDecodeTile) : 1;
+  const int64_t tile = decode_plan_tile(p);
+  const int64_t max_tiles = ceil_div(p.max_kv_len, tile) > 0 ? ceil_div(p.max_kv_len, tile) : 1;
   if (p.kv_chunk > 0) {
     int64_t per = ceil_div(p.max_kv_len, p.kv_chunk);
     return batch * (per > 0 ? per : 1);
@@ -129,6 +135,7 @@ struct PlanArgs {
   int32_t kv_chunk;
   int32_t target_items;
   int32_t block_tokens;
+  int32_t tile;  // decode, automatic chunks: tokens per tile
 };
 
 struct DecodeArgs {

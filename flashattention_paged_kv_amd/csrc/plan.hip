@@ -6,7 +6,7 @@
 // One workgroup of 1024 threads: block reductions / scans over the requests,
 // then an item table written in parallel.
 //
-// Decode, automatic: the requests' 32-token tiles, laid end to end, are cut
+// Decode, automatic: the requests' tiles, laid end to end, are cut
 // into at most target_items equal chunks (target_items = the items whose
 // waves the device holds at once), so the launch runs in one pass and every
 // workgroup streams the same amount of KV.  A chunk is a short list of
@@ -107,14 +107,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   int64_t carry = 0;
 
   if (a.mode == PKV_DECODE && a.kv_chunk == 0) {
-    // Balanced chunks: the requests' 32-token tiles laid end to end (request
+    // Balanced chunks: the requests' tiles (a.tile tokens) laid end to end (request
     // b at global tiles [o_b, o_b + t_b)) are cut into chunks of C tiles,
     // C = ceil(T / target); a chunk is one workgroup and holds the request
     // segments it overlaps, so every workgroup streams the same amount of KV.
     int32_t* goff = ws + a.tmp_off;  // [B+1] global tile offset of each request
     for (int base = 0; base < B; base += blockDim.x) {
       const int b = base + threadIdx.x;
-      const int64_t t = b < B ? (clamp_len(a.seq_lens[b], a.max_kv_len) + kDecodeTile - 1) / kDecodeTile : 0;
+      const int64_t t = b < B ? (clamp_len(a.seq_lens[b], a.max_kv_len) + a.tile - 1) / a.tile : 0;
       int64_t tot;
       const int64_t ex = block_exclusive_scan(t, sh, &tot);
       if (b < B) goff[b] = (int32_t)(carry + ex);
@@ -165,8 +165,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         const int64_t cc = o / C + sgi;
         const int64_t g0 = o > cc * C ? o : cc * C;
         const int64_t g1 = o + t < (cc + 1) * C ? o + t : (cc + 1) * C;
-        const int kb = (int)((g0 - o) * kDecodeTile);
-        const int ke = (int)((g1 - o) * kDecodeTile < L ? (g1 - o) * kDecodeTile : L);
+        const int kb = (int)((g0 - o) * a.tile);
+        const int ke = (int)((g1 - o) * a.tile < L ? (g1 - o) * a.tile : L);
         items[first + sgi] = make_int4(b, kb, ke, n > 1 ? first + sgi : -1);
         seg_chunk[first + sgi] = (int32_t)cc;
       }

@@ -17,7 +17,9 @@ Decode rule (tile = 32 tokens):
   otherwise the number of items whose waves the device holds at once (the
   library queries the decode kernel's occupancy; it is an input here and the
   GPU plan records it in its header).
-* automatic (kv_chunk = 0), balanced chunks: request b occupies global tiles
+* automatic (kv_chunk = 0), balanced chunks over tiles of ``tile`` tokens
+  (the decode kernel's tile: 32 for bf16 K/V, 64 for 8-bit; "32" below
+  stands for it in this mode): request b occupies global tiles
   [o_b, o_b + tiles_b) with o the exclusive prefix sum of tiles, T = Σ tiles_b.
   Chunk size C = max(1, ceil(T / target_items)); nchunks = max(1, ceil(T / C)).
   Chunk c covers global tiles [c·C, (c+1)·C).  Request b is cut into the
@@ -37,7 +39,7 @@ Decode rule (tile = 32 tokens):
   otherwise segment s of request b owns partial slot split_off[b] + s, with
   split_off the exclusive prefix sum of segments per request.
 * capacity (host-visible, never exceeded):
-  automatic: min(target_items + B, B · max(1, ceil(max_kv_len / 32)));
+  automatic: min(target_items + B, B · max(1, ceil(max_kv_len / tile)));
   fixed: B · max(1, ceil(max_kv_len / kv_chunk)).
 
 Extend rule: rows of a work item are (head, token) pairs of one kv head,
@@ -65,17 +67,21 @@ def decode_target_items(num_kv_heads: int, group: int, split_target: int, reside
     return max(1, _ceil_div(split_target, units) if split_target > 0 else resident_items)
 
 
-def decode_capacity(batch: int, max_kv_len: int, target_items: int, kv_chunk: int = 0) -> int:
+def decode_capacity(batch: int, max_kv_len: int, target_items: int, kv_chunk: int = 0,
+                    tile: int = DECODE_TILE) -> int:
     if kv_chunk > 0:
         return batch * max(1, _ceil_div(max_kv_len, kv_chunk))
-    max_tiles = max(1, _ceil_div(max_kv_len, DECODE_TILE))
+    max_tiles = max(1, _ceil_div(max_kv_len, tile))
     return min(target_items + batch, batch * max_tiles)
 
 
-def plan_decode(seq_lens, max_kv_len: int, target_items: int, kv_chunk: int = 0) -> Dict:
+def plan_decode(seq_lens, max_kv_len: int, target_items: int, kv_chunk: int = 0,
+                tile: int = DECODE_TILE) -> Dict:
     L = [int(x) for x in np.clip(np.asarray(seq_lens, dtype=np.int64), 0, max_kv_len)]
     B = len(L)
-    tiles = [_ceil_div(x, DECODE_TILE) for x in L]
+    if kv_chunk > 0:
+        tile = DECODE_TILE
+    tiles = [_ceil_div(x, tile) for x in L]
     items, seg_chunk = [], []
     splits = []
     if kv_chunk > 0:
@@ -109,7 +115,7 @@ def plan_decode(seq_lens, max_kv_len: int, target_items: int, kv_chunk: int = 0)
             for s, c in enumerate(range(first_c, last_c + 1)):
                 g0 = max(o, c * chunk)
                 g1 = min(o + tiles[b], (c + 1) * chunk)
-                items.append([b, (g0 - o) * DECODE_TILE, min((g1 - o) * DECODE_TILE, L[b]), s])
+                items.append([b, (g0 - o) * tile, min((g1 - o) * tile, L[b]), s])
                 seg_chunk.append(c)
             o += tiles[b]
         chunk_tab = [next((i for i, c in enumerate(seg_chunk) if c >= cc), len(items))
@@ -120,9 +126,9 @@ def plan_decode(seq_lens, max_kv_len: int, target_items: int, kv_chunk: int = 0)
     for it in items:  # segment index -> partial slot, or -1 for a whole request
         b, s = it[0], it[3]
         it[3] = split_off[b] + s if splits[b] > 1 else -1
-    cap = decode_capacity(B, max_kv_len, target_items, kv_chunk)
+    cap = decode_capacity(B, max_kv_len, target_items, kv_chunk, tile)
     assert len(items) <= cap
-    return {"chunk_tiles": chunk, "splits": np.array(splits, np.int64),
+    return {"chunk_tiles": chunk, "tile": tile, "splits": np.array(splits, np.int64),
             "split_off": np.array(split_off, np.int64), "target_items": target_items,
             "items": np.array(items, np.int64).reshape(-1, 4), "capacity": cap,
             "nchunks": nchunks, "chunk_tab": np.array(chunk_tab, np.int64)}

@@ -130,13 +130,15 @@ def test_workspace_does_not_grow_with_square_of_length(lib):
 
 def test_capacity_matches_oracle_formula(lib):
     from oracle.plan import decode_capacity, decode_target_items, extend_capacity
-    for (hq, hkv, maxl, chunk, tgt, B) in [(32, 8, 4097, 0, 4096, 64), (64, 8, 131073, 0, 4096, 8),
-                                           (32, 8, 5000, 64, 0, 37), (40, 2, 700, 0, 64, 5),
-                                           (32, 8, 4097, 0, 100, 64)]:
-        p = pkv.Params(hq, hkv, 128, 16, maxl, kv_chunk=chunk, split_target=tgt)
+    for (hq, hkv, maxl, chunk, tgt, B, fp8) in [(32, 8, 4097, 0, 4096, 64, False), (64, 8, 131073, 0, 4096, 8, False),
+                                                (32, 8, 5000, 64, 0, 37, False), (40, 2, 700, 0, 64, 5, False),
+                                                (32, 8, 4097, 0, 100, 64, False), (32, 8, 4097, 0, 100, 64, True),
+                                                (32, 8, 300, 0, 40000, 64, True)]:
+        extra = dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=64, q_block=1) if fp8 else {}
+        p = pkv.Params(hq, hkv, 128, 16, maxl, kv_chunk=chunk, split_target=tgt, **extra)
         rc, ws, sc = _ws(lib, p, batch=B)
         target = decode_target_items(hkv, hq // hkv, tgt, 1)
-        cap = decode_capacity(B, maxl, target, chunk)
+        cap = decode_capacity(B, maxl, target, chunk, 64 if fp8 else 32)
         assert sc >= cap * hq * 129 * 4
         assert ws >= (16 + B + 1 + 4 * cap) * 4
     p = pkv.Params(32, 8, 128, 16, 4096)

@@ -168,12 +168,15 @@ def test_plan_matches_oracle_rederivation_bit_for_bit():
     torch = torch_mod()
     pkv = _pkv()
     rng = np.random.default_rng(11)
-    for kv_chunk, target in ((0, 0), (0, 100), (64, 0), (0, 50000)):
+    for kv_chunk, target, fp8 in ((0, 0, False), (0, 100, False), (64, 0, False), (0, 50000, False),
+                                  (0, 0, True), (0, 300, True), (96, 0, True)):
         B = 37
         max_kv = 5000
         L = rng.integers(0, max_kv + 1, size=B).astype(np.int32)
         L[5] = max_kv + 100  # clamped
-        params = pkv.Params(32, 8, 128, 16, max_kv_len=max_kv, kv_chunk=kv_chunk, split_target=target)
+        extra = dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=64, q_block=1) if fp8 else {}
+        params = pkv.Params(32, 8, 128, 16, max_kv_len=max_kv, kv_chunk=kv_chunk, split_target=target, **extra)
+        tile = 64 if fp8 else 32
         plan = pkv.plan_metadata(params, pkv.PKV_DECODE, dev_i32(L))
         torch.cuda.synchronize()
         ws = plan.workspace.cpu().numpy().view(np.int32)
@@ -181,7 +184,7 @@ def test_plan_matches_oracle_rederivation_bit_for_bit():
             assert ws[5] == oracle.decode_target_items(8, 4, target, 0)
         else:
             assert 1 <= ws[5]  # the device's resident items
-        ref = oracle.plan_decode(L, max_kv, int(ws[5]), kv_chunk=kv_chunk)
+        ref = oracle.plan_decode(L, max_kv, int(ws[5]), kv_chunk=kv_chunk, tile=tile)
         n = ws[2]
         items_off = -(-(16 + B + 1) // 4) * 4
         items = ws[items_off:items_off + 4 * n].reshape(-1, 4)

@@ -95,9 +95,9 @@ def test_sage_p_quantisation_changes_little():
 
 
 # ---------------------------------------------------------------- plan
-@pytest.mark.parametrize("kv_chunk", [0, 32, 96])
+@pytest.mark.parametrize("kv_chunk,tile", [(0, 32), (0, 64), (32, 32), (96, 32)])
 @pytest.mark.parametrize("seed", range(4))
-def test_decode_plan_invariants(seed, kv_chunk):
+def test_decode_plan_invariants(seed, kv_chunk, tile):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 40))
     max_kv = int(rng.integers(1, 5000))
@@ -105,11 +105,11 @@ def test_decode_plan_invariants(seed, kv_chunk):
     L[rng.integers(0, B)] = max_kv + 77  # beyond the bound: must be clamped
     Hkv, G = 8, int(rng.choice([1, 4, 8, 20]))
     target = oracle.decode_target_items(Hkv, G, int(rng.integers(1, 9000)), 512)
-    plan = oracle.plan_decode(L, max_kv, target, kv_chunk=kv_chunk)
+    plan = oracle.plan_decode(L, max_kv, target, kv_chunk=kv_chunk, tile=tile)
     items = plan["items"]
     assert len(items) <= plan["capacity"]
     Lc = np.minimum(L, max_kv)
-    tiles = -(-Lc // oracle.DECODE_TILE)
+    tiles = -(-Lc // tile)
     parts = []
     lengths = items[:, 2] - items[:, 1]
     tab = plan["chunk_tab"]
@@ -123,7 +123,7 @@ def test_decode_plan_invariants(seed, kv_chunk):
         # balanced chunks: every chunk but the last holds exactly C tiles, the
         # last at most C; C is the smallest size giving <= target chunks
         c, T = plan["chunk_tiles"], int(tiles.sum())
-        seg_tiles = -(-lengths // oracle.DECODE_TILE)
+        seg_tiles = -(-lengths // tile)
         per_chunk = [int(seg_tiles[tab[k]:tab[k + 1]].sum()) for k in range(plan["nchunks"])]
         assert sum(per_chunk) == T
         if T:
@@ -135,7 +135,7 @@ def test_decode_plan_invariants(seed, kv_chunk):
         starts = np.concatenate([[0], np.cumsum(tiles)])
         for k in range(plan["nchunks"]):
             for i in range(tab[k], tab[k + 1]):
-                g0 = starts[items[i, 0]] + items[i, 1] // oracle.DECODE_TILE
+                g0 = starts[items[i, 0]] + items[i, 1] // tile
                 if seg_tiles[i]:
                     assert k * c <= g0 and g0 + seg_tiles[i] <= (k + 1) * c
     for b in range(B):
@@ -144,7 +144,7 @@ def test_decode_plan_invariants(seed, kv_chunk):
         assert len(mine) == plan["splits"][b] >= 1
         assert mine[0, 1] == 0 and mine[-1, 2] == Lc[b]
         assert np.all(mine[1:, 1] == mine[:-1, 2])  # contiguous, in order
-        assert np.all(mine[:, 1] % oracle.DECODE_TILE == 0)
+        assert np.all(mine[:, 1] % tile == 0)
         if Lc[b] > 0:
             assert np.all(mine[:, 2] > mine[:, 1])  # no empty split
         if len(mine) == 1:
