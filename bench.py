@@ -46,10 +46,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "flashattention_paged_kv_amd", "csrc")
 
 KERNEL_SOURCES = {
-    "decode_bf16": ["decode_bf16.hip", "device_common.h"],
-    "long_decode_bf16": ["decode_bf16.hip", "device_common.h"],
-    "decode_fp8": ["decode_fp8.hip", "device_common.h"],
-    "extend_bf16": ["extend_bf16.hip", "device_common.h"],
+    "decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
+    "long_decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
+    "decode_fp8": ["decode_fp8.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
+    "extend_bf16": ["extend_bf16.hip", "plan.hip", "device_common.h"],
 }
 
 
