@@ -187,9 +187,12 @@ __device__ __forceinline__ void zero_rows_past_end(char* stage, int t0, int kv_e
   }
 }
 
-// Per-lane LDS byte offsets of the Vᵀ transpose reads for each 32-channel block:
-// key 4 jj + i16/4 (its swizzle is the same for every 16-key step and +8), the
-// chunk pair of channel 32 db + dsub + 4 (i16 % 4); key steps are immediate offsets.
+// Per-lane LDS byte offsets of the Vᵀ transpose reads for each 32-channel block,
+// measured from a stage's K tile: key 4 jj + i16/4 (its swizzle is the same for
+// every 16-key step and +8), the chunk pair of channel 32 db + dsub + 4 (i16 % 4).
+// The V tiles' distance from the K tiles is folded in here and hidden from the
+// optimiser, so the stage and key-step parts of every read stay below 64 KiB
+// and are encoded as the instruction's immediate offset.
 template <int D>
 __device__ __forceinline__ void v_read_bases(int (&vb)[D / 32], int lane) {
   const int g16 = lane >> 4, i16 = lane & 15;
@@ -197,7 +200,7 @@ __device__ __forceinline__ void v_read_bases(int (&vb)[D / 32], int lane) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
-    vb[db] = v_off<D>(key, col >> 3) + ((col & 7) << 1);
+    vb[db] = opaque(ExtSmem<D>::VOFF + v_off<D>(key, col >> 3) + ((col & 7) << 1));
   }
 }
 
@@ -254,17 +257,22 @@ __device__ __forceinline__ void qk_tile(RowState<D>& rs, u32x4 (&pop)[4], const 
     __builtin_amdgcn_sched_barrier(0);
   }
   if (MASKED) {
+    // key t0 + 32 kb + 8 (r/4) + 4 jh + r%4 is visible iff its offset from
+    // t0 + 4 jh is <= lim: one subtraction, then compares with constants
+    const int lim = pos - t0 - 4 * jh;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * jh + (r & 3);
-        s[kb][r] = key <= pos ? s[kb][r] : kNegInf;
-      }
+      for (int r = 0; r < 16; ++r) s[kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) <= lim ? s[kb][r] : kNegInf;
   }
-  float mx = fmaxf(s[0][0], s[1][0]);
+  // row max: two chains of three-input maxima
+  float mx0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]), mx1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+  for (int r = 3; r < 15; r += 2) {
+    mx0 = fmaxf(fmaxf(mx0, s[0][r]), s[0][r + 1]);
+    mx1 = fmaxf(fmaxf(mx1, s[1][r]), s[1][r + 1]);
+  }
+  float mx = fmaxf(fmaxf(mx0, s[0][15]), fmaxf(mx1, s[1][15]));
   mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
   // lazy rescale: the reference max moves only when a row's max exceeds it by
   // more than 8 (log2 units), so exp2(s - m) <= 256 while acc and l keep
@@ -298,7 +306,7 @@ template <int D>
 __device__ __forceinline__ void pv_tile(RowState<D>& rs, const u32x4 (&pop)[4], const char* cur,
                                         const int (&vbase_off)[D / 32]) {
   constexpr int DB = D / 32;
-  const char* vt = cur + ExtSmem<D>::VOFF;
+  const char* vt = cur;  // the V tile's offset is part of vbase_off
   // operands of MFMA n = DB ks2 + db are read one key step (DB MFMAs) ahead;
   // the sched_barriers keep that order
   constexpr int NM = 4 * DB;
