@@ -154,6 +154,19 @@ __device__ __forceinline__ void finish_segment8(const DecodeArgs& a, int b, int 
   }
 }
 
+// Empty segments (requests with no KV) in [from, to): the epilogue of an
+// empty sum, so O = v_mean (0 without it) and lse = -inf.
+__device__ __forceinline__ void finish_empty8(const DecodeArgs& a, SegWindow& w, int from, int to, int s1, int g,
+                                              int h, bool head_ok, int j, int lane) {
+  floatx4 zero[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) zero[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int s = from; s < to; ++s) {
+    const TileCursor e = seg_at(a, w, s, s1, lane);
+    finish_segment8(a, e.b, g, e.part, kNegInf, 0.f, zero, h, head_ok, j);
+  }
+}
+
 // One chunk (the request segments [s0, s1)) for one unit (kv head g,
 // 16-head group), its 64-token tiles walked as one stream as in the bf16
 // decode: while tile i is computed the rows of tile i+1 are in flight and
@@ -181,7 +194,7 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
   TileCursor C = seg_at(a, w, s0, s1, lane);
   C.t0 -= kTile8;
   C = next_tile<kTile8>(a, w, C, s1, lane);
-  finish_empty<D>(a, w, s0, C.seg, s1, h, head_ok, j, lane);
+  finish_empty8(a, w, s0, C.seg, s1, g, h, head_ok, j, lane);
   if (C.seg >= s1) return;
 
   i32x8 qop;
@@ -268,7 +281,7 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
     S = next_tile<kTile8>(a, w, S, s1, lane);
     if (C.seg == prev.seg) return true;
     finish_segment8(a, prev.b, g, prev.part, m, lpart, acc, h, head_ok, j);
-    finish_empty<D>(a, w, prev.seg + 1, C.seg, s1, h, head_ok, j, lane);
+    finish_empty8(a, w, prev.seg + 1, C.seg, s1, g, h, head_ok, j, lane);
     if (C.seg >= s1) return false;
     load_q8(a, qop, qscale, C.b, h, head_ok, j);
     m = kNegInf;

@@ -164,6 +164,38 @@ def test_zero_length_request_gives_zero_and_minus_inf():
     assert_bf16_close(o, ro, "zero-length row")
 
 
+def test_chunks_of_more_than_64_segments():
+    """Few, long chunks over many short requests: each chunk holds ~100 request
+    segments, so the kernels' per-wave segment records are reloaded mid-stream,
+    and every seventh request is empty."""
+    spec = Spec("manyseg", "decode", 300, 8, 2, 128, 16, (0, 60), 1)
+    hb = make_host_batch(spec, 21)
+    seq = hb.layout.seq_lens.copy()
+    seq[::7] = 0
+    # units = 2 (two kv heads, one 16-head group each): 3 chunks
+    o, lse, plan, _ = run_decode(hb, split_target=6, seq_lens_override=seq)
+    ws = plan.workspace.cpu().numpy().view(np.int32)
+    assert ws[6] == 3 and ws[2] > 3 * 64
+    ro, rlse = oracle_decode(hb, seq=seq)
+    assert_bf16_close(o, ro, "many segments per chunk")
+    assert_lse_close(lse, rlse)
+    assert np.all(o[::7] == 0) and np.all(np.isneginf(lse[::7]))
+
+
+def test_long_run_of_empty_requests():
+    """150 consecutive empty requests share one global tile offset, so they all
+    land in one chunk (with the segments around them)."""
+    lens = [3000, 2500, 40] + [0] * 150 + [1800, 33, 700]
+    spec = Spec("empties", "decode", len(lens), 32, 8, 128, 16, [max(x - 1, 0) for x in lens], 1)
+    hb = make_host_batch(spec, 22)
+    seq = np.asarray(lens, dtype=np.int32)
+    o, lse, _, _ = run_decode(hb, seq_lens_override=seq)
+    ro, rlse = oracle_decode(hb, seq=seq)
+    assert_bf16_close(o, ro, "empty run")
+    assert_lse_close(lse, rlse)
+    assert np.all(o[3:153] == 0) and np.all(np.isneginf(lse[3:153]))
+
+
 def test_plan_matches_oracle_rederivation_bit_for_bit():
     torch = torch_mod()
     pkv = _pkv()

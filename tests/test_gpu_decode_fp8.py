@@ -15,7 +15,7 @@ def _pkv():
     return pkv
 
 
-def run_fp8(hb, kv_chunk=0, v_mean=None, sm_scale=None):
+def run_fp8(hb, kv_chunk=0, v_mean=None, sm_scale=None, split_target=0, seq_lens=None):
     torch = torch_mod()
     pkv = _pkv()
     lay = hb.layout
@@ -24,8 +24,10 @@ def run_fp8(hb, kv_chunk=0, v_mean=None, sm_scale=None):
     v_pool = dev_u8(pool_before_store(hb.v_codes, lay.new_slots, fill=0x7F))
     params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
                         max_kv_len=lay.req_to_token.shape[1], kv_dtype=pkv.PKV_FP8_E4M3,
-                        q_block=spec.q_block, k_block=spec.k_block, kv_chunk=kv_chunk)
-    seq, rtt = dev_i32(lay.seq_lens), dev_i32(lay.req_to_token)
+                        q_block=spec.q_block, k_block=spec.k_block, kv_chunk=kv_chunk,
+                        split_target=split_target)
+    seq = dev_i32(lay.seq_lens if seq_lens is None else seq_lens)
+    rtt = dev_i32(lay.req_to_token)
     plan = pkv.plan_metadata(params, pkv.PKV_DECODE, seq)
     pkv.kv_store(params, k_pool, v_pool, dev_u8(hb.k_new_codes), dev_u8(hb.v_new_codes), dev_i32(lay.new_slots))
     lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
@@ -36,9 +38,10 @@ def run_fp8(hb, kv_chunk=0, v_mean=None, sm_scale=None):
     return host(out), lse.cpu().numpy().astype(np.float64)
 
 
-def oracle_fp8(hb, v_mean=None, sm_scale=None):
+def oracle_fp8(hb, v_mean=None, sm_scale=None, seq_lens=None):
     lay = hb.layout
-    return oracle.sage_decode(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens, hb.sfq, hb.sfk,
+    seq = lay.seq_lens if seq_lens is None else seq_lens
+    return oracle.sage_decode(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, seq, hb.sfq, hb.sfk,
                               hb.sfv, lay.spec.k_block, sm_scale=sm_scale, v_mean=v_mean)
 
 
@@ -66,6 +69,26 @@ def test_fp8_split_merge_and_v_mean():
     ro, rlse = oracle_fp8(hb, v_mean=vm)
     assert rel_l2(o1, ro) <= FP8_REL_L2 and rel_l2(o2, ro) <= FP8_REL_L2
     assert np.abs(l1 - rlse).max() <= 1e-3
+
+
+def test_fp8_many_segments_and_empty_requests_with_v_mean():
+    """Three long chunks over 300 short requests (~100 segments each, so the
+    segment records are reloaded mid-stream); every seventh request is empty
+    and gets O = v_mean, lse = -inf, as in the oracle's epilogue."""
+    spec = Spec("f8_manyseg", "decode", 300, 8, 2, 128, 16, (0, 120), 1, dtype="fp8", k_block=64)
+    hb = make_host_batch(spec, 23)
+    seq = hb.layout.seq_lens.copy()
+    seq[::7] = 0
+    vm = np.random.default_rng(1).uniform(-1, 1, size=hb.sfv.shape).astype(np.float32)
+    o, lse = run_fp8(hb, v_mean=vm, split_target=6, seq_lens=seq)
+    ro, rlse = oracle_fp8(hb, v_mean=vm, seq_lens=seq)
+    assert rel_l2(o, ro) <= FP8_REL_L2
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.abs(lse[fin] - rlse[fin]).max() <= 1e-3
+    G = spec.num_q_heads // spec.num_kv_heads
+    want = np.repeat(vm[::7], G, axis=1)
+    np.testing.assert_allclose(o[::7], want, rtol=1e-2, atol=1e-2)
 
 
 def test_fp8_constant_scores_closed_form():
