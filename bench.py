@@ -172,19 +172,20 @@ class DecodeRunner:
         self.kv_bytes_per_layer = tokens * spec.num_kv_heads * spec.head_dim * 2 * esize
         self.work_per_step = self.kv_bytes_per_layer * layers
 
-    def step(self, events=None):
+    def pre(self):
+        """The once-per-step work: the plan and every layer's K/V store."""
         pkv, db = self.pkv, self.db
-        plan = pkv.plan_metadata(self.params, pkv.PKV_DECODE, db.seq_lens, workspace=self.ws)
+        self.plan = pkv.plan_metadata(self.params, pkv.PKV_DECODE, db.seq_lens, workspace=self.ws)
         for l in range(self.layers):
             pkv.kv_store(self.params, db.k_pools[l], db.v_pools[l], db.k_new[l], db.v_new[l], db.new_slots)
-        if events is not None:
-            events[0].record()
+
+    def attn(self):
+        """Every layer's attention call, back to back."""
+        pkv, db = self.pkv, self.db
         for l in range(self.layers):
-            pkv.attn_decode(self.params, db.q, db.k_pools[l], db.v_pools[l], db.req_to_token, db.seq_lens, plan,
+            pkv.attn_decode(self.params, db.q, db.k_pools[l], db.v_pools[l], db.req_to_token, db.seq_lens, self.plan,
                             scratch=self.scratch, out=self.out[l], lse=self.lse,
                             sfq=db.sfq, sfk=db.sfk, sfv=db.sfv)
-        if events is not None:
-            events[1].record()
 
     def describe(self):
         s = self.spec
@@ -257,19 +258,20 @@ class ExtendRunner:
         self.flops_per_layer = 4 * spec.head_dim * spec.num_q_heads * pairs
         self.work_per_step = self.flops_per_layer * layers
 
-    def step(self, events=None):
+    def pre(self):
+        """The once-per-step work: the plan and every layer's K/V store."""
         pkv, db = self.pkv, self.db
-        plan = pkv.plan_metadata(self.params, pkv.PKV_EXTEND, db.seq_lens, db.cu_seqlens_q, total_q=self.total_q,
-                                 workspace=self.ws)
+        self.plan = pkv.plan_metadata(self.params, pkv.PKV_EXTEND, db.seq_lens, db.cu_seqlens_q,
+                                      total_q=self.total_q, workspace=self.ws)
         for l in range(self.layers):
             pkv.kv_store(self.params, db.k_pools[l], db.v_pools[l], db.k_new[l], db.v_new[l], db.new_slots)
-        if events is not None:
-            events[0].record()
+
+    def attn(self):
+        """Every layer's attention call, back to back."""
+        pkv, db = self.pkv, self.db
         for l in range(self.layers):
             pkv.attn_extend(self.params, db.q, db.k_pools[l], db.v_pools[l], db.req_to_token, db.seq_lens,
-                            db.cu_seqlens_q, plan, out=self.out[l], lse=self.lse)
-        if events is not None:
-            events[1].record()
+                            db.cu_seqlens_q, self.plan, out=self.out[l], lse=self.lse)
 
     def describe(self):
         s = self.spec
@@ -292,10 +294,38 @@ UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "decode_fp8": "GB/s"
 DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "decode_fp8": 4, "extend_bf16": 4}
 
 
-def measure(name, steps, warmup, layers, torch, pkv, workloads):
+def capture(runner, torch):
+    """The step as two HIP graphs (plan + stores, then the attention calls),
+    captured once after an eager run on a side stream; replays reuse every
+    buffer, as a serving loop does for its decode steps."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        runner.pre()
+        runner.attn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g_pre, g_attn = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_pre):
+        runner.pre()
+    with torch.cuda.graph(g_attn):
+        runner.attn()
+    torch.cuda.synchronize()
+    return g_pre.replay, g_attn.replay
+
+
+def measure(name, steps, warmup, layers, torch, pkv, workloads, graph=False):
     runner = RUNNERS[name](name, layers or DEFAULT_LAYERS[name], torch, pkv, workloads)
+    pre, attn = runner.pre, runner.attn
     for _ in range(warmup):
-        runner.step()
+        pre()
+        attn()
+    torch.cuda.synchronize()
+    if graph:
+        pre, attn = capture(runner, torch)
+        for _ in range(warmup):
+            pre()
+            attn()
     torch.cuda.synchronize()
     # one event pair per step around the attention block (all layers back to back):
     # every event record adds a few microseconds of queue gap, so none sit between launches
@@ -304,7 +334,10 @@ def measure(name, steps, warmup, layers, torch, pkv, workloads):
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        runner.step(blocks[i])
+        pre()
+        blocks[i][0].record()
+        attn()
+        blocks[i][1].record()
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
@@ -325,6 +358,9 @@ def main():
                     help="comma list of workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as captured HIP graphs (plan + stores, then the attention calls) "
+                         "instead of launching every kernel from Python")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the 1 GiB copy (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV files (host only)")
@@ -347,18 +383,21 @@ def main():
     import workloads
 
     pkv.load_library()  # fails loudly when the HIP library is missing
-    runner, ms, value, roof = measure(args.workload, args.steps, args.warmup, args.layers, torch, pkv, workloads)
+    graph = args.graph
+    runner, ms, value, roof = measure(args.workload, args.steps, args.warmup, args.layers, torch, pkv, workloads,
+                                      graph=graph)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": UNITS[args.workload], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3" if getattr(runner, "fp8", False) else "bf16",
-        "data": "synthetic", "config": runner.describe(), "roofline": roof,
+        "data": "synthetic", "config": runner.describe(), "launch": "hip_graph" if graph else "eager",
+        "roofline": roof,
     }
     secondary = {}
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
         try:
             r2, ms2, v2, roof2 = measure(name, max(args.steps // 2, 5), max(args.warmup // 2, 2), 0, torch, pkv,
-                                         workloads)
+                                         workloads, graph=graph)
             secondary[name] = {"value": round(v2, 2), "unit": UNITS[name], "ms_per_step": round(ms2, 4),
                                "config": r2.describe(), "roofline": roof2}
             del r2
