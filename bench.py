@@ -46,6 +46,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "flashattention_paged_kv_amd", "csrc")
 
 KERNEL_SOURCES = {
+    "decode_n4_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "long_decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "decode_fp8": ["decode_fp8.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
@@ -79,6 +80,7 @@ CALL_KERNELS = {
     "decode_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
     "long_decode_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
     "decode_fp8": ("decode_fp8_kernel", "decode_merge_kernel"),
+    "decode_n4_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
     "extend_bf16": ("extend_bf16_kernel",),
 }
 COPY_BYTES = 1 << 30
@@ -159,14 +161,16 @@ class DecodeRunner:
         lay = self.db.layout
         self.layers = layers
         kw = dict(kv_dtype=pkv.PKV_FP8_E4M3, q_block=spec.q_block, k_block=spec.k_block) if self.fp8 else {}
+        self.q_len = int(lay.new_lens[0])  # new tokens per request
         self.params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
-                                 max_kv_len=lay.req_to_token.shape[1], **kw)
+                                 max_kv_len=lay.req_to_token.shape[1], decode_q_len=self.q_len, **kw)
         ws_bytes, sc_bytes = pkv.workspace_size(self.params, pkv.PKV_DECODE, spec.batch)
         self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
         self.scratch = torch.empty(max(sc_bytes, 16), dtype=torch.uint8, device="cuda")
-        self.out = [torch.empty((spec.batch, spec.num_q_heads, spec.head_dim), dtype=torch.bfloat16, device="cuda")
+        rows = spec.batch * self.q_len
+        self.out = [torch.empty((rows, spec.num_q_heads, spec.head_dim), dtype=torch.bfloat16, device="cuda")
                     for _ in range(layers)]
-        self.lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((rows, spec.num_q_heads), dtype=torch.float32, device="cuda")
         esize = 1 if self.fp8 else 2
         tokens = int(lay.seq_lens.astype("int64").sum())
         self.kv_bytes_per_layer = tokens * spec.num_kv_heads * spec.head_dim * 2 * esize
@@ -191,7 +195,8 @@ class DecodeRunner:
         s = self.spec
         lo, hi = s.prefix
         return {"workload": s.name, "batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
-                "head_dim": s.head_dim, "page_size": s.page_size, "cached_len": f"U[{lo},{hi}] + 1 new token",
+                "head_dim": s.head_dim, "page_size": s.page_size,
+                "cached_len": f"U[{lo},{hi}] + {self.q_len} new token{'s' if self.q_len > 1 else ''}",
                 "kv_dtype": "fp8_e4m3" if self.fp8 else "bf16", "layers_per_step": self.layers,
                 "kv_bytes_per_layer": self.kv_bytes_per_layer}
 
@@ -227,7 +232,8 @@ class DecodeRunner:
                 oracle.sage_decode(q[b:b + 1], kp, vp, rtt, L, sfq[b:b + 1], sfk[b:b + 1], sfv[b:b + 1],
                                    k_block=spec.k_block)
             else:
-                oracle.paged_attention(q[b:b + 1], kp, vp, rtt, L, [0, 1])
+                nq = self.q_len
+                oracle.paged_attention(q[b * nq:(b + 1) * nq], kp, vp, rtt, L, [0, nq])
             done_bytes += int(L[0]) * spec.num_kv_heads * spec.head_dim * 2 * (1 if self.fp8 else 2)
             n += 1
         dt = time.perf_counter() - t0
@@ -289,9 +295,10 @@ class ExtendRunner:
 
 
 RUNNERS = {"decode_bf16": DecodeRunner, "long_decode_bf16": DecodeRunner, "decode_fp8": DecodeRunner,
-           "extend_bf16": ExtendRunner}
-UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "decode_fp8": "GB/s", "extend_bf16": "TFLOP/s"}
-DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "decode_fp8": 4, "extend_bf16": 4}
+           "decode_n4_bf16": DecodeRunner, "extend_bf16": ExtendRunner}
+UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "decode_fp8": "GB/s", "decode_n4_bf16": "GB/s",
+         "extend_bf16": "TFLOP/s"}
+DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "decode_fp8": 4, "decode_n4_bf16": 4, "extend_bf16": 4}
 
 
 def capture(runner, torch):
@@ -354,7 +361,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_bf16", choices=sorted(RUNNERS))
     ap.add_argument("--layers", type=int, default=0, help="layers (distinct K/V pools) per step")
-    ap.add_argument("--secondary", default="extend_bf16,long_decode_bf16,decode_fp8",
+    ap.add_argument("--secondary", default="extend_bf16,long_decode_bf16,decode_fp8,decode_n4_bf16",
                     help="comma list of workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -37,12 +37,13 @@ class Params(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("q_block", ctypes.c_int32),
                 ("k_block", ctypes.c_int32), ("max_kv_len", ctypes.c_int32),
-                ("kv_chunk", ctypes.c_int32), ("split_target", ctypes.c_int32)]
+                ("kv_chunk", ctypes.c_int32), ("split_target", ctypes.c_int32),
+                ("decode_q_len", ctypes.c_int32)]
 
     def __init__(self, num_q_heads, num_kv_heads, head_dim, page_size, max_kv_len,
-                 kv_dtype=PKV_BF16, q_block=0, k_block=0, kv_chunk=0, split_target=0):
+                 kv_dtype=PKV_BF16, q_block=0, k_block=0, kv_chunk=0, split_target=0, decode_q_len=0):
         super().__init__(num_q_heads, num_kv_heads, head_dim, page_size, kv_dtype, q_block,
-                         k_block, max_kv_len, kv_chunk, split_target)
+                         k_block, max_kv_len, kv_chunk, split_target, decode_q_len)
 
 
 _P = ctypes.c_void_p
@@ -167,6 +168,9 @@ def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan:
     B = seq_lens.shape[0]
     if plan.mode != PKV_DECODE or plan.batch != B:
         raise ValueError("plan was not made by plan_metadata(PKV_DECODE) for this batch")
+    n = max(params.decode_q_len, 1)
+    if q.shape[0] != B * n:
+        raise ValueError(f"q must have batch * decode_q_len = {B * n} rows")
     if params.kv_dtype == PKV_FP8_E4M3 and sfk is not None:
         nblk = -(-params.max_kv_len // params.k_block)
         if tuple(sfk.shape) != (B, params.num_kv_heads, nblk):

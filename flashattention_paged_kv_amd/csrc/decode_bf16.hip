@@ -91,14 +91,17 @@ __device__ __forceinline__ void compute_tile(const KVTile<D>& t, const u32x4 (&q
   float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m, mx);  // finite: token t0 of the tile is always in range
-  const float alpha = exp2_fast(m - m_new);
+  // -inf only for a column that has seen no key yet (a new token whose causal
+  // limit lies below this tile); it then keeps zero weight
+  const float m_new = fmaxf(m, mx);
+  const float alpha = m_new == kNegInf ? 1.f : exp2_fast(m - m_new);
+  const float m_use = m_new == kNegInf ? 0.f : m_new;
   m = m_new;
   float p[8];
   float ps = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    p[i] = exp2_fast(sc[i] - m_new);
+    p[i] = exp2_fast(sc[i] - m_use);
     ps += p[i];
   }
   lpart = lpart * alpha + ps;
@@ -122,12 +125,15 @@ __device__ __forceinline__ void compute_tile(const KVTile<D>& t, const u32x4 (&q
 
 }  // namespace
 
+// Q of output row (request b, new token qi), query head h, as the B operand.
 template <int D>
-__device__ __forceinline__ void load_q(const DecodeArgs& a, u32x4 (&qop)[D / 32], int b, int h, bool head_ok,
+__device__ __forceinline__ void load_q(const DecodeArgs& a, u32x4 (&qop)[D / 32], int b, int qi, int h, bool head_ok,
                                        int j) {
+  qi = opaque(qi);
   h = opaque(h);
   j = opaque(j);
-  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (head_ok ? h : 0)) * D;
+  const uint16_t* qrow =
+      static_cast<const uint16_t*>(a.q) + (((int64_t)b * a.q_len + (head_ok ? qi : 0)) * a.hq + (head_ok ? h : 0)) * D;
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb) qop[kb] = head_ok ? ldg16(qrow + 32 * kb + 8 * j) : z;
@@ -137,7 +143,8 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, u32x4 (&qop)[D / 32]
 // request covered by one segment, else the fp32 partial and its log2-sum-exp.
 template <int D>
 __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int part, float m, float lpart,
-                                               const floatx4 (&acc)[8], int h, bool head_ok, int j) {
+                                               const floatx4 (&acc)[8], int qi, int h, bool head_ok, int j) {
+  qi = opaque(qi);
   h = opaque(h);
   j = opaque(j);
   float l = lpart + __shfl_xor(lpart, 16);
@@ -147,7 +154,7 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int p
   const float lse2 = l > 0.f ? m + __log2f(l) : kNegInf;
   if (part < 0) {
     if (head_ok && rows_ok) {
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.hq + h) * D;
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + (((int64_t)b * a.q_len + qi) * a.hq + h) * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         u32x4 w;
@@ -156,11 +163,11 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int p
         stg16(orow + 32 * j + 8 * r, w);
       }
     }
-    if (head_ok && j == 0 && a.lse) a.lse[(int64_t)b * a.hq + h] = lse2 * kLn2;
+    if (head_ok && j == 0 && a.lse) a.lse[((int64_t)b * a.q_len + qi) * a.hq + h] = lse2 * kLn2;
     return;
   }
   if (head_ok && rows_ok) {
-    float* po = a.part_o + ((int64_t)part * a.hq + h) * D;
+    float* po = a.part_o + (((int64_t)part * a.q_len + qi) * a.hq + h) * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       floatx4 w0 = {acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
@@ -169,7 +176,7 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int p
       *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r + 4) = w1;
     }
   }
-  if (head_ok && j == 0) a.part_lse[(int64_t)part * a.hq + h] = lse2;
+  if (head_ok && j == 0) a.part_lse[((int64_t)part * a.q_len + qi) * a.hq + h] = lse2;
 }
 
 // One chunk (the request segments [s0, s1)) for one unit (kv head g,
@@ -181,12 +188,14 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int p
 // previous one is written out and the online-softmax state restarts.
 template <int D>
 __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int s0, int s1, int unit, int4* win_rec,
-                                             int* win_row) {
+                                             int2* win_req) {
   const int g = unit / a.head_groups, hg = unit - g * a.head_groups;
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, j = lane >> 4;
-  const int hl = hg * 16 + l16;
-  const bool head_ok = hl < a.group;
+  // MFMA column l16 of this unit = (new token qi, query head hl of kv head g)
+  const int col = hg * 16 + l16;
+  const int qi = col / a.group, hl = col - qi * a.group;
+  const bool head_ok = qi < a.q_len;
   const int h = g * a.group + hl;
   const uint32_t row_elems = (uint32_t)a.hkv * D;
   const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * D;
@@ -195,17 +204,17 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int s0, int s1
 
   SegWindow w;
   w.rec = win_rec;
-  w.row = win_row;
+  w.req = win_req;
   load_window(a, w, s0, s1, lane);
   // first non-empty segment
   TileCursor C = seg_at(a, w, s0, s1, lane);
   C.t0 -= kDecodeTile;
   C = next_tile<kDecodeTile>(a, w, C, s1, lane);
-  finish_empty<D>(a, w, s0, C.seg, s1, h, head_ok, j, lane);
+  finish_empty<D>(a, w, s0, C.seg, s1, qi, h, head_ok, j, lane);
   if (C.seg >= s1) return;
 
   u32x4 qop[D / 32];
-  load_q<D>(a, qop, C.b, h, head_ok, j);
+  load_q<D>(a, qop, C.b, qi, h, head_ok, j);
   float m = kNegInf, lpart = 0.f;
   floatx4 acc[8];
 #pragma unroll
@@ -226,10 +235,10 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int s0, int s1
     L = S;
     S = next_tile<kDecodeTile>(a, w, S, s1, lane);
     if (C.seg == prev.seg) return true;
-    finish_segment<D>(a, prev.b, prev.part, m, lpart, acc, h, head_ok, j);
-    finish_empty<D>(a, w, prev.seg + 1, C.seg, s1, h, head_ok, j, lane);
+    finish_segment<D>(a, prev.b, prev.part, m, lpart, acc, qi, h, head_ok, j);
+    finish_empty<D>(a, w, prev.seg + 1, C.seg, s1, qi, h, head_ok, j, lane);
     if (C.seg >= s1) return false;
-    load_q<D>(a, qop, C.b, h, head_ok, j);
+    load_q<D>(a, qop, C.b, qi, h, head_ok, j);
     m = kNegInf;
     lpart = 0.f;
 #pragma unroll
@@ -241,12 +250,12 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int s0, int s1
     s_even = tile_slot(rtt_of(S), S.t0, S.kv_end, last, lane);
     load_tile<D>(tb, s_odd, kbase, vbase, row_elems, lane);
     __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
-    compute_tile<D>(ta, qop, C.t0, C.kv_end, a.scale_log2, m, lpart, acc, lane);
+    compute_tile<D>(ta, qop, C.t0, min(C.kv_end, C.lim + qi + 1), a.scale_log2, m, lpart, acc, lane);
     if (!advance()) break;
     s_odd = tile_slot(rtt_of(S), S.t0, S.kv_end, last, lane);
     load_tile<D>(ta, s_even, kbase, vbase, row_elems, lane);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<D>(tb, qop, C.t0, C.kv_end, a.scale_log2, m, lpart, acc, lane);
+    compute_tile<D>(tb, qop, C.t0, min(C.kv_end, C.lim + qi + 1), a.scale_log2, m, lpart, acc, lane);
     if (!advance()) break;
   }
 }
@@ -266,13 +275,13 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tab = ws[WS_CHUNK_TAB];
   const int s0 = tab ? ws[tab + c] : c, s1 = tab ? ws[tab + c + 1] : c + 1;
   __shared__ int4 win_rec[WPB][64];
-  __shared__ int win_row[WPB][64];
-  decode_chunk<D>(a, s0, s1, unit, win_rec[wv], win_row[wv]);
+  __shared__ int2 win_req[WPB][64];
+  decode_chunk<D>(a, s0, s1, unit, win_rec[wv], win_req[wv]);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int32_t batch, hipStream_t s) {
   if (batch <= 0) return hipSuccess;
-  dim3 grid((unsigned)batch, (unsigned)a.hq);
+  dim3 grid((unsigned)batch, (unsigned)(a.q_len * a.hq));
   if (head_dim == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(kMergeThreads), 0, s, a);
   else hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();

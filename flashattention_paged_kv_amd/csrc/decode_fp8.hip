@@ -173,7 +173,7 @@ __device__ __forceinline__ void finish_empty8(const DecodeArgs& a, SegWindow& w,
 // the slots of tile i+2 were requested before them, whichever segments the
 // tiles belong to.
 __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, int s1, int unit, int4* win_rec,
-                                                 int* win_row) {
+                                                 int2* win_req) {
   constexpr int D = 128;
   const int g = unit / a.head_groups, hg = unit - g * a.head_groups;
   const int lane = threadIdx.x & 63;
@@ -188,7 +188,7 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
 
   SegWindow w;
   w.rec = win_rec;
-  w.row = win_row;
+  w.req = win_req;
   load_window(a, w, s0, s1, lane);
   // first non-empty segment
   TileCursor C = seg_at(a, w, s0, s1, lane);
@@ -317,8 +317,8 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tab = ws[WS_CHUNK_TAB];
   const int s0 = tab ? ws[tab + c] : c, s1 = tab ? ws[tab + c + 1] : c + 1;
   __shared__ int4 win_rec[WPB][64];
-  __shared__ int win_row[WPB][64];
-  decode_fp8_chunk(a, s0, s1, unit, win_rec[wv], win_row[wv]);
+  __shared__ int2 win_req[WPB][64];
+  decode_fp8_chunk(a, s0, s1, unit, win_rec[wv], win_req[wv]);
 }
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch, hipStream_t s) {

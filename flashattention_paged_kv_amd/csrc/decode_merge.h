@@ -14,7 +14,8 @@
 
 namespace pkv {
 
-// One wave per (request, query head) of a request with more than one split.
+// One wave per (request, output row of the request, query head) of a request
+// with more than one split.
 // Lane = (split group sg = lane / 16, channel group c = lane % 16 holding 8
 // channels): the lane folds splits sg, sg + 4, ... into a running
 // log-sum-exp (max M, weight sum T, weighted O), with every split's loads
@@ -24,7 +25,9 @@ constexpr int kMergeThreads = 64;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
-  const int b = blockIdx.x, h = blockIdx.y;
+  // y = (new token i) * Hq + query head: the request's output row i, head h
+  const int b = blockIdx.x, y = blockIdx.y;
+  const int rows = a.q_len * a.hq;
   const int32_t* __restrict__ req = a.ws + a.req_off;
   const int num = a.ws[WS_NUM_ITEMS];
   const int s0 = req[b];
@@ -36,8 +39,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   float M = kNegInf, T = 0.f;
   floatx4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
   for (int s = sg; s < ns; s += 4) {
-    const float ls = a.part_lse[(int64_t)(s0 + s) * a.hq + h];
-    const float* po = a.part_o + ((int64_t)(s0 + s) * a.hq + h) * D + 8 * (d_ok ? cg : 0);
+    const float ls = a.part_lse[(int64_t)(s0 + s) * rows + y];
+    const float* po = a.part_o + ((int64_t)(s0 + s) * rows + y) * D + 8 * (d_ok ? cg : 0);
     const floatx4 p0 = *reinterpret_cast<const floatx4*>(po), p1 = *reinterpret_cast<const floatx4*>(po + 4);
     if (ls == kNegInf) continue;  // an empty split contributes nothing
     if (ls > M) {
@@ -76,9 +79,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
     w[1] = pack_bf16x2(o0[2] * inv, o0[3] * inv);
     w[2] = pack_bf16x2(o1[0] * inv, o1[1] * inv);
     w[3] = pack_bf16x2(o1[2] * inv, o1[3] * inv);
-    stg16(static_cast<uint16_t*>(a.out) + ((int64_t)b * a.hq + h) * D + 8 * cg, w);
+    stg16(static_cast<uint16_t*>(a.out) + ((int64_t)b * rows + y) * D + 8 * cg, w);
   }
-  if (cg == 0 && a.lse) a.lse[(int64_t)b * a.hq + h] = T > 0.f ? (M + __log2f(T)) * kLn2 : kNegInf;
+  if (cg == 0 && a.lse) a.lse[(int64_t)b * rows + y] = T > 0.f ? (M + __log2f(T)) * kLn2 : kNegInf;
 }
 
 }  // namespace pkv

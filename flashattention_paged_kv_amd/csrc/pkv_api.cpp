@@ -52,6 +52,12 @@ int check_params(const pkv_params* p, int mode) {
   if (p->kv_chunk < 0 || p->kv_chunk % pkv::kDecodeTile != 0)
     return fail(PKV_EINVAL, "kv_chunk=%d must be 0 or a positive multiple of %d", p->kv_chunk, pkv::kDecodeTile);
   if (p->split_target < 0) return fail(PKV_EINVAL, "split_target=%d must be >= 0", p->split_target);
+  if (p->decode_q_len < 0 || p->decode_q_len > 64)
+    return fail(PKV_EINVAL, "decode_q_len=%d must be in [0, 64]", p->decode_q_len);
+  if (p->decode_q_len > 1 && mode != PKV_DECODE)
+    return fail(PKV_EINVAL, "decode_q_len applies to DECODE plans only (EXTEND takes cu_seqlens_q)");
+  if (p->decode_q_len > 1 && p->kv_dtype != PKV_BF16)
+    return fail(PKV_EUNSUPPORTED, "decode_q_len > 1 is unsupported with kv_dtype=%d", p->kv_dtype);
   if (p->kv_dtype == PKV_BF16) {
     // block sizes only exist for the 8-bit recipe: reject them like an
     // inapplicable plan input (FlashInfer Sage page, code §2)
@@ -249,8 +255,11 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
   a.req_off = w.req_off;
   a.hq = params->num_q_heads;
   a.hkv = params->num_kv_heads;
+  a.seq_lens = seq_lens;
+  a.max_kv_len = params->max_kv_len;
+  a.q_len = pkv::decode_q_len(*params);
   a.group = group;
-  a.head_groups = (int32_t)pkv::ceil_div(group, 16);
+  a.head_groups = (int32_t)pkv::ceil_div((int64_t)a.q_len * group, 16);
   a.k_block = params->k_block;
   a.sfk_stride = fp8 ? (int32_t)pkv::ceil_div(params->max_kv_len, params->k_block) : 0;
   a.scale_log2 = sm_scale * 1.4426950408889634f;

@@ -51,9 +51,13 @@ inline int64_t next_pow2(int64_t x) {
   return p;
 }
 
-// Decode work units per split: one per (kv head, group of up to 16 query heads).
+// New tokens per request in a decode call (1 unless several are verified at once).
+inline int decode_q_len(const pkv_params& p) { return p.decode_q_len > 1 ? p.decode_q_len : 1; }
+
+// Decode work units per split: one per (kv head, group of up to 16 of its
+// (new token, query head) columns).
 inline int64_t decode_units(const pkv_params& p) {
-  return (int64_t)p.num_kv_heads * ceil_div(p.num_q_heads / p.num_kv_heads, 16);
+  return (int64_t)p.num_kv_heads * ceil_div((int64_t)decode_q_len(p) * (p.num_q_heads / p.num_kv_heads), 16);
 }
 
 // Split items the automatic chunk is sized for: by default the number of
@@ -115,9 +119,10 @@ struct DecodeScratch {
 inline DecodeScratch decode_scratch(const pkv_params& p, int64_t batch, int64_t target_items) {
   DecodeScratch s;
   const int64_t cap = decode_capacity(p, batch, target_items);
-  s.part_o_bytes = align_up(cap * p.num_q_heads * p.head_dim * (int64_t)sizeof(float), 256);
+  const int64_t rows = (int64_t)decode_q_len(p) * p.num_q_heads;  // partial rows per split
+  s.part_o_bytes = align_up(cap * rows * p.head_dim * (int64_t)sizeof(float), 256);
   s.part_lse_off = s.part_o_bytes;
-  s.total_bytes = s.part_o_bytes + align_up(cap * p.num_q_heads * (int64_t)sizeof(float), 256);
+  s.total_bytes = s.part_o_bytes + align_up(cap * rows * (int64_t)sizeof(float), 256);
   return s;
 }
 
@@ -157,7 +162,10 @@ struct DecodeArgs {
   int64_t pool_slots;
   int64_t items_off;
   int64_t req_off;
-  int32_t hq, hkv, group, head_groups;
+  const int32_t* seq_lens;
+  int32_t max_kv_len;
+  int32_t q_len;  // new tokens per request (1 for ordinary decode)
+  int32_t hq, hkv, group, head_groups;  // head_groups: 16-column groups of q_len * group per kv head
   int32_t k_block, sfk_stride;
   float scale_log2;  // sm_scale * log2(e)
 };

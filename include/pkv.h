@@ -98,6 +98,10 @@ typedef struct pkv_params {
   int32_t split_target; /* DECODE automatic mode: waves per call to size splits for; 0 = as many
                            as the current device holds at once (from the kernel's occupancy;
                            256 CUs x 16 when no device is present) */
+  int32_t decode_q_len; /* DECODE: new tokens per request, n in [1, 64] (0 means 1).  With n > 1
+                           (e.g. verifying n drafted tokens) q and out are [B*n, Hq, d], rows
+                           request-major, and new token i of request b attends to keys
+                           0 .. L_b - n + i (bottom-right causal, as EXTEND); bf16 only */
 } pkv_params;
 
 /* Sizes of the plan workspace (written by pkv_plan_metadata, read by the run

@@ -18,7 +18,7 @@ def _pkv():
 
 
 def run_decode(hb, kv_chunk=0, split_target=0, sm_scale=None, req_pool_indices=None, max_kv_len=None,
-               seq_lens_override=None, lse=True):
+               seq_lens_override=None, lse=True, decode_q_len=0):
     """Upload a host batch (new rows poisoned), plan, store, decode; return host (o, lse, plan)."""
     torch = torch_mod()
     pkv = _pkv()
@@ -32,12 +32,12 @@ def run_decode(hb, kv_chunk=0, split_target=0, sm_scale=None, req_pool_indices=N
     seq = lay.seq_lens if seq_lens_override is None else seq_lens_override
     params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
                         max_kv_len=max_kv_len or max(lay.req_to_token.shape[1], 1),
-                        kv_chunk=kv_chunk, split_target=split_target)
+                        kv_chunk=kv_chunk, split_target=split_target, decode_q_len=decode_q_len)
     seq_d = dev_i32(seq)
     rtt = dev_i32(lay.req_to_token)
     plan = pkv.plan_metadata(params, pkv.PKV_DECODE, seq_d)
     pkv.kv_store(params, k_pool, v_pool, k_new, v_new, dev_i32(lay.new_slots))
-    lse_t = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda") if lse else None
+    lse_t = torch.empty((lay.total_q, spec.num_q_heads), dtype=torch.float32, device="cuda") if lse else None
     rpi = None if req_pool_indices is None else dev_i32(req_pool_indices)
     out = pkv.attn_decode(params, dev_bf16(q), k_pool, v_pool, rtt, seq_d, plan, sm_scale=sm_scale,
                           lse=lse_t, req_pool_indices=rpi)
@@ -49,7 +49,7 @@ def oracle_decode(hb, sm_scale=None, seq=None):
     lay = hb.layout
     seq = lay.seq_lens if seq is None else seq
     return oracle.paged_attention(round_bf16(hb.q), round_bf16(hb.k_pool), round_bf16(hb.v_pool),
-                                  lay.req_to_token, seq, np.arange(len(seq) + 1), sm_scale=sm_scale)
+                                  lay.req_to_token, seq, lay.cu_seqlens_q, sm_scale=sm_scale)
 
 
 MEDIUM = Spec("dec_med", "decode", 8, 32, 8, 128, 16, (0, 1500), 1)
@@ -194,6 +194,35 @@ def test_long_run_of_empty_requests():
     assert_bf16_close(o, ro, "empty run")
     assert_lse_close(lse, rlse)
     assert np.all(o[3:153] == 0) and np.all(np.isneginf(lse[3:153]))
+
+
+def test_shared_prefix_pages():
+    """Requests whose page-table rows point at one request's prefix pages (a
+    prefix shared by copy-on-write, as the PagedAttention page describes
+    for block sharing): the kernels follow the table, whatever slots repeat."""
+    spec = Spec("sharedpfx", "decode", 12, 32, 8, 128, 16, (300, 1500), 1)
+    hb = make_host_batch(spec, 24)
+    lay = hb.layout
+    shared = (int(lay.prefix_lens.min()) // 16) * 16
+    lay.req_to_token[1:, :shared] = lay.req_to_token[0, :shared]
+    o, lse, _, _ = run_decode(hb)
+    ro, rlse = oracle_decode(hb)
+    assert_bf16_close(o, ro, "shared prefix")
+    assert_lse_close(lse, rlse)
+
+
+@pytest.mark.parametrize("n,hq,hkv,kv_chunk", [(2, 32, 8, 0), (4, 32, 8, 0), (4, 32, 8, 64), (3, 8, 8, 0),
+                                              (8, 16, 2, 0), (5, 64, 8, 0), (16, 8, 8, 96)])
+def test_several_new_tokens_per_request(n, hq, hkv, kv_chunk):
+    """n new tokens per request in one decode call (a verify step of n drafted
+    tokens): token i sees the cached prefix and new tokens 0..i.  Columns of
+    the MFMA are (token, head) pairs, n * G of them per kv head."""
+    spec = Spec(f"dec_n{n}", "decode", 9, hq, hkv, 128, 16, (0, 900), n)
+    hb = make_host_batch(spec, 30 + n)
+    o, lse, _, _ = run_decode(hb, decode_q_len=n, kv_chunk=kv_chunk)
+    ro, rlse = oracle_decode(hb)
+    assert_bf16_close(o, ro, f"n={n}")
+    assert_lse_close(lse, rlse)
 
 
 def test_plan_matches_oracle_rederivation_bit_for_bit():

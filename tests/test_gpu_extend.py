@@ -107,6 +107,20 @@ def test_page_relabelling_is_bit_invariant_and_deterministic():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def test_shared_prefix_pages():
+    """Every request's page-table row starts with request 0's prefix pages
+    (a shared prompt prefix); new tokens stay in each request's own pages."""
+    spec = Spec("ext_sharedpfx", "extend", 5, 32, 8, 128, 16, (200, 500), (1, 300))
+    hb = make_host_batch(spec, 25)
+    lay = hb.layout
+    shared = (int(lay.prefix_lens.min()) // 16) * 16
+    lay.req_to_token[1:, :shared] = lay.req_to_token[0, :shared]
+    o, lse, _ = run_extend(hb)
+    ro, rlse = oracle_extend(hb)
+    assert_bf16_close(o, ro, "shared prefix")
+    assert_lse_close(lse, rlse)
+
+
 def test_extend_plan_matches_oracle_rederivation():
     torch = torch_mod()
     pkv = _pkv()

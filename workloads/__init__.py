@@ -22,11 +22,14 @@ name                   description
 ``decode_fp8``         B=64, 32/8 heads, d=128, page 16, cached U[1024,8192];
                        E4M3 codes of N(0,1)/scale with per-64-token sfK,
                        per-(b,h) sfQ and per-channel sfV drawn from U[0.5,2]
+``decode_n4_bf16``     as ``decode_bf16`` with 4 new tokens per request
+                       checked in one decode call (a verify step)
 =====================  =====================================================
 
-Every decode workload appends one new token per request: the drawn value is
-the cached length and the attended length is ``cached + 1`` (the new token's
-K/V row is written by ``kv_store`` before attention reads it).
+Decode workloads append n new tokens per request (one unless stated): the
+drawn value is the cached length and the attended length is ``cached + n``
+(the new tokens' K/V rows are written by ``kv_store`` before attention
+reads them).
 """
 from __future__ import annotations
 
@@ -74,12 +77,13 @@ SPECS = {
     "extend_bf16": Spec("extend_bf16", "extend", 16, 32, 8, 128, 16, (0, 2048), (128, 2048)),
     "long_decode_bf16": Spec("long_decode_bf16", "decode", 8, 64, 8, 128, 64,
                              (32768, 131072), 1),
+    "decode_n4_bf16": Spec("decode_n4_bf16", "decode", 64, 32, 8, 128, 16, (512, 4096), 4),
     "decode_fp8": Spec("decode_fp8", "decode", 64, 32, 8, 128, 16, (1024, 8192), 1,
                        dtype="fp8", k_block=64, q_block=1),
 }
 
 # Index used to derive the seed of each named workload (1000 + index).
-SPEC_INDEX = {"tiny_decode": 1, "tiny_extend": 1, "decode_bf16": 2, "extend_bf16": 3,
+SPEC_INDEX = {"tiny_decode": 1, "tiny_extend": 1, "decode_bf16": 2, "extend_bf16": 3, "decode_n4_bf16": 6,
               "long_decode_bf16": 4, "decode_fp8": 5}
 
 
@@ -136,7 +140,9 @@ def make_layout(spec: Spec, seed: int = 0, rng: Optional[np.random.Generator] = 
     prefix = _draw(rng, spec.prefix, B)
     new = _draw(rng, spec.new, B)
     if spec.mode == "decode":
-        assert np.all(new == 1), "decode appends exactly one token per request"
+        # one new token per request, or the same n for every request (several
+        # tokens checked in one decode call)
+        assert B == 0 or (np.all(new == new[0]) and new[0] >= 1), "decode appends the same n >= 1 tokens per request"
     seq = prefix + new
     pages_per_req = (seq + P - 1) // P
     pages_needed = int(pages_per_req.sum())
