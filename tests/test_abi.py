@@ -50,6 +50,9 @@ def _ws(lib, params, mode=pkv.PKV_DECODE, batch=4, total_q=0):
     (dict(kv_dtype=7), pkv.PKV_EUNSUPPORTED, "kv_dtype=7"),
     (dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=20, q_block=1), pkv.PKV_EINVAL, "k_block=20"),
     (dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=64, q_block=1, head_dim=64), pkv.PKV_EUNSUPPORTED, "head_dim=128"),
+    (dict(decode_q_len=-1), pkv.PKV_EINVAL, "decode_q_len=-1"),
+    (dict(decode_q_len=65), pkv.PKV_EINVAL, "decode_q_len=65"),
+    (dict(decode_q_len=4, kv_dtype=pkv.PKV_FP8_E4M3, k_block=64, q_block=1), pkv.PKV_EUNSUPPORTED, "decode_q_len > 1"),
 ])
 def test_params_validation(lib, kw, code, msg):
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_kv_len=4096)
@@ -58,6 +61,18 @@ def test_params_validation(lib, kw, code, msg):
     rc, _, _ = _ws(lib, p)
     assert rc == code
     assert msg in pkv.last_error()
+
+
+def test_decode_q_len_sizes_scratch_per_token_and_is_decode_only(lib):
+    p1 = pkv.Params(32, 8, 128, 16, 4096, split_target=2048)
+    p4 = pkv.Params(32, 8, 128, 16, 4096, split_target=2048, decode_q_len=4)
+    _, _, sc1 = _ws(lib, p1, batch=16)
+    rc, _, sc4 = _ws(lib, p4, batch=16)
+    assert rc == pkv.PKV_OK
+    # same units (4 tokens x 4 heads fill one 16-column group), 4x the partial rows
+    assert sc4 >= 4 * sc1 - 4 * 512
+    rc, _, _ = _ws(lib, p4, mode=pkv.PKV_EXTEND, batch=16, total_q=64)
+    assert rc == pkv.PKV_EINVAL and "DECODE plans only" in pkv.last_error()
 
 
 def test_fp8_extend_is_rejected_at_plan_time(lib):
