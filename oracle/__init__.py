@@ -33,6 +33,11 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
   example; power-of-two sfV scaling).  The difference between quantising P
   against the final row max (here) and a running max (an online kernel) is
   bounded only by the stated fp8 tolerance: parity unpinned beyond it.
+* ``sage_extend``: pinned by reductions to pinned functions (one new token
+  per request equals ``sage_decode``; every row equals ``sage_decode`` on
+  the request cut at that row's causal limit; unit scales and P
+  unquantised equal ``paged_attention``; q8 = 0 gives sfV·mean(V8) over the
+  visible keys).  Same running-max caveat as ``sage_decode``.
 * ``plan_decode`` / ``plan_extend``: the split heuristic is a design choice,
   not from the pages; pinned by invariants (every token covered once, in
   order; bounds on tile multiples; capacity; the chunk is the smallest that
@@ -42,14 +47,14 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
 from .attention import paged_attention
 from .merge import lse_merge
 from .e4m3 import e4m3_encode, e4m3_decode, E4M3_MAX
-from .sage import sage_decode
+from .sage import sage_decode, sage_extend
 from .plan import plan_decode, plan_extend, decode_target_items, DECODE_TILE, EXTEND_BLOCK_M
 from .kv_store import kv_store
 from .memory import score_matrix_bytes
 
 __all__ = [
     "paged_attention", "lse_merge", "e4m3_encode",
-    "e4m3_decode", "E4M3_MAX", "sage_decode", "plan_decode", "plan_extend",
+    "e4m3_decode", "E4M3_MAX", "sage_decode", "sage_extend", "plan_decode", "plan_extend",
     "DECODE_TILE", "EXTEND_BLOCK_M", "decode_target_items", "kv_store",
     "score_matrix_bytes",
 ]

@@ -80,3 +80,53 @@ def sage_decode(q8, k8_pool, v8_pool, req_to_token, seq_lens, sfq, sfk, sfv,
             out[b, h] = o
             lse[b, h] = m + math.log(l)
     return out, lse
+
+
+def sage_extend(q8, k8_pool, v8_pool, req_to_token, seq_lens, cu_seqlens_q, sfq, sfk, sfv,
+                k_block: int, sm_scale: Optional[float] = None, v_mean=None,
+                quantize_p: bool = True, req_pool_indices=None):
+    """The same 8-bit formula for the new-token rows of an extend batch.
+
+    q8: [T, Hq, d] codes, rows request-major (cu_seqlens_q); sfq: [T, Hq] (one
+    Q block per row, the page's default q_block = 1); sfk [B, Hkv, nblk], sfv
+    and v_mean [B, Hkv, d].  New token i of request b sits at absolute
+    position p_b + i (p_b = L_b - n_b) and sees keys 0 .. p_b + i (causal,
+    bottom-right aligned, as the bf16 extend).  Returns (o [T, Hq, d],
+    lse [T, Hq]) in float64.
+    """
+    q8 = np.asarray(q8)
+    T, Hq, d = q8.shape
+    Hkv = k8_pool.shape[1]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    out = np.zeros((T, Hq, d), dtype=np.float64)
+    lse = np.full((T, Hq), -np.inf, dtype=np.float64)
+    for b in range(len(seq_lens)):
+        row = b if req_pool_indices is None else int(req_pool_indices[b])
+        q0, q1 = int(cu[b]), int(cu[b + 1])
+        L = int(seq_lens[b])
+        p0 = L - (q1 - q0)
+        slots = np.asarray(req_to_token[row, :L], dtype=np.int64)
+        K = e4m3_decode(np.asarray(k8_pool)[slots])  # [L, Hkv, d] exact
+        V = e4m3_decode(np.asarray(v8_pool)[slots])
+        blk = np.arange(L) // k_block
+        for t in range(q0, q1):
+            vis = p0 + (t - q0) + 1  # keys 0 .. p_b + i
+            for h in range(Hq):
+                g = h // G
+                dots = K[:vis, g, :] @ e4m3_decode(q8[t, h])
+                S = sm_scale * float(sfq[t, h]) * np.asarray(sfk[b, g, blk[:vis]], np.float64) * dots
+                m = S.max()
+                p = np.exp(S - m)
+                l = p.sum()
+                P8 = 448.0 * p
+                if quantize_p:
+                    P8 = e4m3_decode(e4m3_encode(P8))
+                o = np.asarray(sfv[b, g], np.float64) * (P8 @ V[:vis, g, :]) / (448.0 * l)
+                if v_mean is not None:
+                    o = o + np.asarray(v_mean[b, g], np.float64)
+                out[t, h] = o
+                lse[t, h] = m + math.log(l)
+    return out, lse

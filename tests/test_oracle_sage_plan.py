@@ -194,3 +194,63 @@ def test_score_memory_figures_from_the_flashattention_page():
     for c in g["cases"]:
         got = oracle.score_matrix_bytes(c["seq_len"], c["elem_bytes"], c["heads"], c["batch"])
         assert got == c["approx_bytes"]
+
+
+# ---------------------------------------------------------------- 8-bit extend
+FP8_EXT = Spec("f8_ext", "extend", 3, 8, 2, 64, 4, (0, 40), (1, 9), dtype="fp8", k_block=16)
+
+
+def _sage_ext(hb, **kw):
+    lay = hb.layout
+    return oracle.sage_extend(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens,
+                              lay.cu_seqlens_q, hb.sfq, hb.sfk, hb.sfv, FP8_EXT.k_block, **kw)
+
+
+def test_sage_extend_rows_equal_sage_decode_on_the_causal_prefix():
+    """Row i of request b is the decode formula over keys 0..p_b+i with that row's sfQ."""
+    hb = make_host_batch(FP8_EXT, 0)
+    lay = hb.layout
+    o, lse = _sage_ext(hb)
+    for b in range(FP8_EXT.batch):
+        q0, q1 = int(lay.cu_seqlens_q[b]), int(lay.cu_seqlens_q[b + 1])
+        p0 = int(lay.seq_lens[b]) - (q1 - q0)
+        for t in range(q0, q1):
+            od, ld = oracle.sage_decode(hb.q_codes[t:t + 1], hb.k_codes, hb.v_codes, lay.req_to_token[b:b + 1],
+                                        [p0 + t - q0 + 1], hb.sfq[t:t + 1], hb.sfk[b:b + 1], hb.sfv[b:b + 1],
+                                        FP8_EXT.k_block)
+            assert np.array_equal(o[t], od[0]) and np.array_equal(lse[t], ld[0])
+
+
+def test_sage_extend_unit_scales_unquantised_p_is_plain_causal_attention():
+    hb = make_host_batch(FP8_EXT, 1)
+    lay = hb.layout
+    hb.sfq[:] = 1.0
+    hb.sfk[:] = 1.0
+    hb.sfv[:] = 1.0
+    o, lse = _sage_ext(hb, quantize_p=False)
+    q = oracle.e4m3_decode(hb.q_codes)
+    k = oracle.e4m3_decode(hb.k_codes)
+    v = oracle.e4m3_decode(hb.v_codes)
+    ro, rlse = oracle.paged_attention(q, k, v, lay.req_to_token, lay.seq_lens, lay.cu_seqlens_q)
+    assert np.abs(o - ro).max() <= 1e-12 and np.abs(lse - rlse).max() <= 1e-12
+
+
+def test_sage_extend_zero_queries_give_mean_over_visible_keys():
+    """q8 = 0: every visible key gets p = 1, P8 = 448 exactly, so O = sfV * mean(V8)
+    over keys 0..p_b+i, a different mean for every row."""
+    hb = make_host_batch(FP8_EXT, 2)
+    lay = hb.layout
+    hb.q_codes[:] = 0
+    o, lse = _sage_ext(hb)
+    v = oracle.e4m3_decode(hb.v_codes)
+    G = FP8_EXT.num_q_heads // FP8_EXT.num_kv_heads
+    for b in range(FP8_EXT.batch):
+        q0, q1 = int(lay.cu_seqlens_q[b]), int(lay.cu_seqlens_q[b + 1])
+        p0 = int(lay.seq_lens[b]) - (q1 - q0)
+        for t in range(q0, q1):
+            vis = p0 + t - q0 + 1
+            slots = lay.req_to_token[b, :vis]
+            for h in range(FP8_EXT.num_q_heads):
+                want = hb.sfv[b, h // G] * v[slots, h // G].mean(axis=0)
+                np.testing.assert_allclose(o[t, h], want, rtol=1e-12, atol=1e-12)
+                assert abs(lse[t, h] - math.log(vis)) <= 1e-12

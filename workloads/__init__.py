@@ -242,12 +242,13 @@ def make_host_batch(spec: Spec, seed: int = 0, poison: bool = True,
         B = spec.batch
         lo, hi = spec.scale_range
         nblk = max((lay.max_kv_len + spec.k_block - 1) // spec.k_block, 1)
-        sfq = rng.uniform(lo, hi, size=(B, Hq)).astype(np.float32)
+        # sfQ: one scale per (request, head) for decode, per (new-token row,
+        # head) for extend (q_block = 1)
+        sfq = rng.uniform(lo, hi, size=(T if spec.mode == "extend" else B, Hq)).astype(np.float32)
         sfk = rng.uniform(lo, hi, size=(B, Hkv, nblk)).astype(np.float32)
         sfv = rng.uniform(lo, hi, size=(B, Hkv, d)).astype(np.float32)
-        # q rows of request b: decode has exactly one row per request
         req_of_row = np.repeat(np.arange(B), lay.new_lens)
-        q_codes = e4m3_codes(q / sfq[req_of_row][:, :, None])
+        q_codes = e4m3_codes(q / (sfq if spec.mode == "extend" else sfq[req_of_row])[:, :, None])
         owner = np.where(used, lay.slot_owner, 0)
         blk = np.where(used, lay.slot_pos, 0) // spec.k_block
         ks = sfk[owner, :, blk]  # [S, Hkv]
@@ -348,7 +349,7 @@ def make_device_batch(spec: Spec, seed: int = 0, device="cuda", layers: int = 1,
         B = spec.batch
         lo, hi = spec.scale_range
         nblk = max((lay.max_kv_len + spec.k_block - 1) // spec.k_block, 1)
-        sfq = rng.uniform(lo, hi, size=(B, Hq)).astype(np.float32)
+        sfq = rng.uniform(lo, hi, size=(T if spec.mode == "extend" else B, Hq)).astype(np.float32)
         sfk = rng.uniform(lo, hi, size=(B, Hkv, nblk)).astype(np.float32)
         sfv = rng.uniform(lo, hi, size=(B, Hkv, d)).astype(np.float32)
         db.sfq, db.sfk, db.sfv = (torch.from_numpy(x).to(dev) for x in (sfq, sfk, sfv))
@@ -359,7 +360,8 @@ def make_device_batch(spec: Spec, seed: int = 0, device="cuda", layers: int = 1,
         v_scale = db.sfv[owner]  # [S, Hkv, d]
         req_of_row = torch.from_numpy(np.repeat(np.arange(B), lay.new_lens)).to(dev)
         qf = torch.randn((T, Hq, d), generator=g, device=dev, dtype=torch.float32)
-        db.q = (qf / db.sfq[req_of_row][:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        q_scale = db.sfq if spec.mode == "extend" else db.sfq[req_of_row]
+        db.q = (qf / q_scale[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
         for _ in range(layers):
             kf = torch.randn((S, Hkv, d), generator=g, device=dev, dtype=torch.float32)
             kc = (kf / k_scale[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
