@@ -67,7 +67,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_attn_decode.argtypes = [pp, _P, _P, _P, _P, _P, _I64, _P, _I64, _P, _P, _I32, _F,
                                     _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]
     lib.pkv_attn_extend.argtypes = [pp, _P, _P, _P, _P, _P, _I64, _P, _I64, _P, _P, _P, _I32, _I64,
-                                    _F, _P, _SZ, _P, _SZ, _P]
+                                    _F, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]
     for f in ("pkv_workspace_size", "pkv_plan_metadata", "pkv_kv_store", "pkv_attn_decode",
               "pkv_attn_extend", "pkv_version"):
         getattr(lib, f).restype = ctypes.c_int
@@ -199,10 +199,15 @@ def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan:
 
 
 def attn_extend(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, cu_seqlens_q, plan: Plan,
-                out=None, lse=None, sm_scale: Optional[float] = None, req_pool_indices=None):
-    """Causal extend attention: q [total_q, Hq, d] bf16 -> out [total_q, Hq, d] bf16."""
+                out=None, lse=None, sm_scale: Optional[float] = None, req_pool_indices=None,
+                sfq=None, sfk=None, sfv=None, v_mean=None):
+    """Causal extend attention: q [total_q, Hq, d] (bf16, or uint8 E4M3 codes with
+    sfq [total_q, Hq], sfk, sfv and optional v_mean) -> out [total_q, Hq, d] bf16."""
     import torch
-    _need(q, "q", torch.bfloat16, 3)
+    fp8 = params.kv_dtype == PKV_FP8_E4M3
+    _need(q, "q", torch.uint8 if fp8 else torch.bfloat16, 3)
+    for t, nm in ((sfq, "sfq"), (sfk, "sfk"), (sfv, "sfv"), (v_mean, "v_mean")):
+        _need(t, nm, torch.float32)
     _need(req_to_token, "req_to_token", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
@@ -212,6 +217,16 @@ def attn_extend(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, cu_se
     total_q = q.shape[0]
     if plan.mode != PKV_EXTEND or plan.batch != B or plan.total_q != total_q:
         raise ValueError("plan was not made by plan_metadata(PKV_EXTEND) for this batch and total_q")
+    if fp8 and sfk is not None:
+        nblk = -(-params.max_kv_len // params.k_block)
+        if tuple(sfk.shape) != (B, params.num_kv_heads, nblk):
+            raise ValueError(f"sfk must be [B, Hkv, ceil(max_kv_len/k_block)] = {(B, params.num_kv_heads, nblk)}")
+        if sfq is None or tuple(sfq.shape) != (total_q, params.num_q_heads):
+            raise ValueError("sfq must be [total_q, Hq]")
+        if sfv is None or tuple(sfv.shape) != (B, params.num_kv_heads, params.head_dim):
+            raise ValueError("sfv must be [B, Hkv, d]")
+        if v_mean is not None and tuple(v_mean.shape) != (B, params.num_kv_heads, params.head_dim):
+            raise ValueError("v_mean must be [B, Hkv, d]")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, 3)
@@ -221,6 +236,7 @@ def attn_extend(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, cu_se
     ws = plan.workspace
     _check(lib.pkv_attn_extend(ctypes.byref(params), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                k_pool.shape[0], _ptr(req_to_token), req_to_token.shape[1], _ptr(req_pool_indices),
-                               _ptr(seq_lens), _ptr(cu_seqlens_q), B, total_q, float(sm_scale), _ptr(ws),
-                               ws.numel() * ws.element_size(), None, 0, _stream()))
+                               _ptr(seq_lens), _ptr(cu_seqlens_q), B, total_q, float(sm_scale), _ptr(sfq),
+                               _ptr(sfk), _ptr(sfv), _ptr(v_mean), _ptr(ws), ws.numel() * ws.element_size(),
+                               None, 0, _stream()))
     return out

@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "lds_dma.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -87,11 +88,6 @@ __device__ __forceinline__ int v_off(int row, int chunk) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) char lds_char;
-
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(lds_char*)(const_cast<char*>(p));
-}
 
 __device__ __forceinline__ u32x2 lds_read_tr16(const char* base, uint32_t off) {
   // transposing 8-byte LDS read (gfx950): see the kernel header
@@ -102,23 +98,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* base, uint32_t off) {
 
 __device__ __forceinline__ floatx16 mfma32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Global -> LDS loads.  Written as inline assembly so the compiler neither
-// counts them nor orders LDS reads of other stages behind them; the kernel
-// waits for them explicitly (wait_vmem<N>) before publishing a stage.  Each
-// 64-lane instruction writes consecutive LDS bytes from `lds` (M0), lane i at
-// lds + i * size.  M0 is used by nothing else in this kernel.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N <= 15, "vmcnt wait depth");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Row of the tile handled by (wave, load q, lane); the lane writes LDS chunk

@@ -64,11 +64,13 @@ int check_params(const pkv_params* p, int mode) {
     if (p->q_block != 0) return fail(PKV_EINVAL, "q_block is unsupported by a bf16 plan");
     if (p->k_block != 0) return fail(PKV_EINVAL, "k_block is unsupported by a bf16 plan");
   } else if (p->kv_dtype == PKV_FP8_E4M3) {
-    if (mode != PKV_DECODE) return fail(PKV_EUNSUPPORTED, "kv_dtype=fp8_e4m3 is unsupported by an extend plan");
     if (p->head_dim != 128) return fail(PKV_EUNSUPPORTED, "kv_dtype=fp8_e4m3 requires head_dim=128");
     if (p->k_block < 16 || p->k_block % 16 != 0)
       return fail(PKV_EINVAL, "k_block=%d must be a positive multiple of 16", p->k_block);
     if (p->q_block < 1) return fail(PKV_EINVAL, "q_block=%d must be >= 1", p->q_block);
+    if (mode == PKV_EXTEND && p->q_block != 1)
+      return fail(PKV_EUNSUPPORTED, "an fp8_e4m3 extend plan takes one sfQ per row (q_block=1), not q_block=%d",
+                  p->q_block);
   } else {
     return fail(PKV_EUNSUPPORTED, "kv_dtype=%d is unsupported", p->kv_dtype);
   }
@@ -273,11 +275,17 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
 int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void* q, const void* k_pool,
                     const void* v_pool, int64_t pool_slots, const int32_t* req_to_token, int64_t rtt_stride,
                     const int32_t* req_pool_indices, const int32_t* seq_lens, const int32_t* cu_seqlens_q,
-                    int32_t batch, int64_t total_q, float sm_scale, const void* workspace, size_t workspace_bytes,
+                    int32_t batch, int64_t total_q, float sm_scale, const float* sfq, const float* sfk,
+                    const float* sfv, const float* v_mean, const void* workspace, size_t workspace_bytes,
                     void* scratch, size_t scratch_bytes, void* stream) {
   (void)scratch;
   (void)scratch_bytes;
   if (int rc = check_params(params, PKV_EXTEND)) return rc;
+  const bool fp8 = params->kv_dtype == PKV_FP8_E4M3;
+  if (!fp8 && (sfq || sfk || sfv || v_mean))
+    return fail(PKV_EINVAL, "sfq, sfk, sfv and v_mean are unsupported by a bf16 plan");
+  if (fp8 && batch > 0 && total_q > 0 && (!sfq || !sfk || !sfv))
+    return fail(PKV_EINVAL, "the fp8_e4m3 extend needs sfq, sfk and sfv");
   if (batch < 0) return fail(PKV_EINVAL, "batch=%d must be >= 0", batch);
   if (total_q < 0) return fail(PKV_EINVAL, "total_q=%lld must be >= 0", (long long)total_q);
   if (pool_slots < 1 || pool_slots > ((int64_t)1 << 31))
@@ -318,7 +326,15 @@ int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void*
   a.block_tokens = pkv::extend_block_tokens(*params);
   a.max_kv_len = params->max_kv_len;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  return check_launch(pkv::launch_extend_bf16(a, params->head_dim, w.capacity, static_cast<hipStream_t>(stream)),
+  a.sfq = sfq;
+  a.sfk = sfk;
+  a.sfv = sfv;
+  a.v_mean = v_mean;
+  a.k_block = params->k_block;
+  a.sfk_stride = fp8 ? (int32_t)pkv::ceil_div(params->max_kv_len, params->k_block) : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return check_launch(fp8 ? pkv::launch_extend_fp8(a, w.capacity, s)
+                          : pkv::launch_extend_bf16(a, params->head_dim, w.capacity, s),
                       "attn_extend launch");
 }
 

@@ -188,10 +188,17 @@ struct ExtendArgs {
   int32_t hq, hkv, group, block_tokens;
   int32_t max_kv_len;
   float scale_log2;
+  // 8-bit path only
+  const float* sfq;
+  const float* sfk;
+  const float* sfv;
+  const float* v_mean;
+  int32_t k_block, sfk_stride;
 };
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_extend_fp8(const ExtendArgs& a, int64_t capacity, hipStream_t s);
 hipError_t launch_kv_store(void* k_pool, void* v_pool, int64_t pool_slots, const void* k_new,
                            const void* v_new, const int32_t* slots, int64_t num_tokens,
                            int64_t row_bytes, hipStream_t s);

@@ -90,8 +90,8 @@ typedef struct pkv_params {
   int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0 */
   int32_t head_dim;     /* d: 64 or 128 */
   int32_t page_size;    /* power of two in [1, 256]; informational (reads are per token) */
-  int32_t kv_dtype;     /* pkv_dtype; PKV_FP8_E4M3 only for DECODE */
-  int32_t q_block;      /* 8-bit: q rows per sfQ block (DECODE uses one row per request); else 0 */
+  int32_t kv_dtype;     /* pkv_dtype; PKV_FP8_E4M3 needs head_dim 128 (and q_block 1 for EXTEND) */
+  int32_t q_block;      /* 8-bit: q rows per sfQ block (DECODE: one row per request; EXTEND: 1); else 0 */
   int32_t k_block;      /* 8-bit: key positions per sfK block, a multiple of 16; else 0 */
   int32_t max_kv_len;   /* upper bound of seq_lens (>= 1, <= rtt_stride of the run calls) */
   int32_t kv_chunk;     /* DECODE split size in tokens: 0 = automatic, else a multiple of 32 */
@@ -154,16 +154,23 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
                     const void* workspace, size_t workspace_bytes, void* scratch,
                     size_t scratch_bytes, void* stream);
 
-/* EXTEND: causal attention of the total_q new-token rows (q, out:
- * [total_q, Hq, d] bf16) over their request's cached prefix and themselves,
- * bf16 pools.  `workspace` comes from pkv_plan_metadata(PKV_EXTEND) with the
- * same batch and total_q.  `scratch` is not used (may be NULL). */
+/* EXTEND: causal attention of the total_q new-token rows (q: [total_q, Hq, d],
+ * out: [total_q, Hq, d] bf16) over their request's cached prefix and
+ * themselves.  bf16 path: q and pools bf16, sfq/sfk/sfv/v_mean NULL.  8-bit
+ * path (kv_dtype == PKV_FP8_E4M3, q_block == 1): q and pools hold E4M3 bytes
+ * and the Sage formula of pkv_attn_decode applies to every row, with sfq
+ * float [total_q, Hq] (one scale per row), sfk [B, Hkv, ceil(max_kv_len /
+ * k_block)], sfv and v_mean [B, Hkv, d] (v_mean may be NULL); the running
+ * maximum is exact, so no quantised probability exceeds 448.  `workspace`
+ * comes from pkv_plan_metadata(PKV_EXTEND) with the same batch and total_q.
+ * `scratch` is not used (may be NULL). */
 int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void* q,
                     const void* k_pool, const void* v_pool, int64_t pool_slots,
                     const int32_t* req_to_token, int64_t rtt_stride, const int32_t* req_pool_indices,
                     const int32_t* seq_lens, const int32_t* cu_seqlens_q, int32_t batch,
-                    int64_t total_q, float sm_scale, const void* workspace, size_t workspace_bytes,
-                    void* scratch, size_t scratch_bytes, void* stream);
+                    int64_t total_q, float sm_scale, const float* sfq, const float* sfk,
+                    const float* sfv, const float* v_mean, const void* workspace,
+                    size_t workspace_bytes, void* scratch, size_t scratch_bytes, void* stream);
 
 /* Text of the calling thread's last error ("" if none).  Valid until the
  * thread's next pkv_* call. */

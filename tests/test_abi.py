@@ -75,10 +75,15 @@ def test_decode_q_len_sizes_scratch_per_token_and_is_decode_only(lib):
     assert rc == pkv.PKV_EINVAL and "DECODE plans only" in pkv.last_error()
 
 
-def test_fp8_extend_is_rejected_at_plan_time(lib):
-    p = pkv.Params(32, 8, 128, 16, 4096, kv_dtype=pkv.PKV_FP8_E4M3, q_block=1, k_block=64)
+def test_fp8_extend_plans_take_one_sfq_per_row(lib):
+    """The 8-bit extend takes q_block = 1 (the Sage page's default); a larger Q
+    block is rejected when planning, like the page's plan-time checks (code §2)."""
+    p = pkv.Params(32, 8, 128, 16, 4096, kv_dtype=pkv.PKV_FP8_E4M3, q_block=1, k_block=16)
+    rc, ws, _ = _ws(lib, p, mode=pkv.PKV_EXTEND, total_q=100)
+    assert rc == pkv.PKV_OK and ws > 0
+    p = pkv.Params(32, 8, 128, 16, 4096, kv_dtype=pkv.PKV_FP8_E4M3, q_block=64, k_block=64)
     rc, _, _ = _ws(lib, p, mode=pkv.PKV_EXTEND, total_q=100)
-    assert rc == pkv.PKV_EUNSUPPORTED and "unsupported by an extend plan" in pkv.last_error()
+    assert rc == pkv.PKV_EUNSUPPORTED and "q_block=1" in pkv.last_error()
     rc, ws, sc = _ws(lib, p, mode=pkv.PKV_DECODE)
     assert rc == pkv.PKV_OK and ws > 0 and sc > 0
 
@@ -114,8 +119,16 @@ def test_run_call_argument_errors(lib):
     assert rc == pkv.PKV_EINVAL and "16-byte aligned" in pkv.last_error()
     # extend: NULL cu_seqlens_q
     rc = lib.pkv_attn_extend(ctypes.byref(p), fake, None, fake, fake, fake, 100, fake, 4096, None, fake, None, 4,
-                             64, 0.1, fake, 1 << 20, None, 0, None)
+                             64, 0.1, None, None, None, None, fake, 1 << 20, None, 0, None)
     assert rc == pkv.PKV_EINVAL and "cu_seqlens_q" in pkv.last_error()
+    # extend: scales given to a bf16 plan; an 8-bit plan without them
+    rc = lib.pkv_attn_extend(ctypes.byref(p), fake, None, fake, fake, fake, 100, fake, 4096, None, fake, fake, 4,
+                             64, 0.1, fake, None, None, None, fake, 1 << 20, None, 0, None)
+    assert rc == pkv.PKV_EINVAL and "unsupported by a bf16 plan" in pkv.last_error()
+    p8 = pkv.Params(32, 8, 128, 16, 4096, kv_dtype=pkv.PKV_FP8_E4M3, q_block=1, k_block=16)
+    rc = lib.pkv_attn_extend(ctypes.byref(p8), fake, None, fake, fake, fake, 100, fake, 4096, None, fake, fake, 4,
+                             64, 0.1, None, None, None, None, fake, 1 << 20, None, 0, None)
+    assert rc == pkv.PKV_EINVAL and "needs sfq, sfk and sfv" in pkv.last_error()
     # plan: NULL seq_lens, workspace too small
     rc = lib.pkv_plan_metadata(ctypes.byref(p), pkv.PKV_DECODE, 4, 0, None, None, fake, 1 << 20, None)
     assert rc == pkv.PKV_EINVAL and "seq_lens" in pkv.last_error()

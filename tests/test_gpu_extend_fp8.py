@@ -1,0 +1,114 @@
+"""GPU parity of the 8-bit (OCP E4M3) Sage extend against the fp64 oracle of
+the formula, through the C ABI via the ctypes binding."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import FP8_REL_L2, dev_f32, dev_i32, dev_u8, host, rel_l2, torch_mod
+from workloads import Spec, make_host_batch, pool_before_store
+
+pytestmark = pytest.mark.gpu
+
+
+def _pkv():
+    import flashattention_paged_kv_amd as pkv
+    return pkv
+
+
+def run_fp8_extend(hb, v_mean=None, sm_scale=None):
+    torch = torch_mod()
+    pkv = _pkv()
+    lay = hb.layout
+    spec = lay.spec
+    k_pool = dev_u8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F))
+    v_pool = dev_u8(pool_before_store(hb.v_codes, lay.new_slots, fill=0x7F))
+    params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                        max_kv_len=lay.req_to_token.shape[1], kv_dtype=pkv.PKV_FP8_E4M3,
+                        q_block=1, k_block=spec.k_block)
+    seq, cu, rtt = dev_i32(lay.seq_lens), dev_i32(lay.cu_seqlens_q), dev_i32(lay.req_to_token)
+    plan = pkv.plan_metadata(params, pkv.PKV_EXTEND, seq, cu, total_q=lay.total_q)
+    pkv.kv_store(params, k_pool, v_pool, dev_u8(hb.k_new_codes), dev_u8(hb.v_new_codes), dev_i32(lay.new_slots))
+    lse = torch.empty((lay.total_q, spec.num_q_heads), dtype=torch.float32, device="cuda")
+    out = pkv.attn_extend(params, dev_u8(hb.q_codes), k_pool, v_pool, rtt, seq, cu, plan, lse=lse,
+                          sm_scale=sm_scale, sfq=dev_f32(hb.sfq), sfk=dev_f32(hb.sfk), sfv=dev_f32(hb.sfv),
+                          v_mean=None if v_mean is None else dev_f32(v_mean))
+    torch.cuda.synchronize()
+    return host(out), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_fp8_extend(hb, v_mean=None, sm_scale=None):
+    lay = hb.layout
+    return oracle.sage_extend(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens, lay.cu_seqlens_q,
+                              hb.sfq, hb.sfk, hb.sfv, lay.spec.k_block, sm_scale=sm_scale, v_mean=v_mean)
+
+
+SMALL = Spec("f8_ext_small", "extend", 4, 32, 8, 128, 16, (0, 300), (1, 300), dtype="fp8", k_block=16)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("k_block", [16, 64])
+def test_fp8_extend_matches_sage_oracle(seed, k_block):
+    hb = make_host_batch(replace(SMALL, k_block=k_block), seed)
+    o, lse = run_fp8_extend(hb)
+    ro, rlse = oracle_fp8_extend(hb)
+    assert np.all(np.isfinite(o))
+    assert rel_l2(o, ro) <= FP8_REL_L2, rel_l2(o, ro)
+    assert np.abs(lse - rlse).max() <= 1e-3
+
+
+@pytest.mark.parametrize("hq,hkv,page", [(8, 8, 1), (64, 8, 64), (12, 4, 16)])
+def test_fp8_extend_head_groupings_and_pages(hq, hkv, page):
+    spec = Spec(f"f8_ext_{hq}_{hkv}_{page}", "extend", 3, hq, hkv, 128, page, (0, 200), (1, 150), dtype="fp8",
+                k_block=16)
+    hb = make_host_batch(spec, 3)
+    o, lse = run_fp8_extend(hb)
+    ro, rlse = oracle_fp8_extend(hb)
+    assert rel_l2(o, ro) <= FP8_REL_L2
+    assert np.abs(lse - rlse).max() <= 1e-3
+
+
+def test_fp8_extend_v_mean_and_scale():
+    hb = make_host_batch(SMALL, 4)
+    vm = np.random.default_rng(0).uniform(-1, 1, size=hb.sfv.shape).astype(np.float32)
+    o, lse = run_fp8_extend(hb, v_mean=vm, sm_scale=0.05)
+    ro, rlse = oracle_fp8_extend(hb, v_mean=vm, sm_scale=0.05)
+    assert rel_l2(o, ro) <= FP8_REL_L2
+    assert np.abs(lse - rlse).max() <= 1e-3
+
+
+def test_fp8_extend_zero_queries_closed_form():
+    """q8 = 0: p = 1 for every visible key, P8 = 448 exactly, so O = sfV * mean(V8)
+    over each row's visible keys and lse = ln(visible keys)."""
+    hb = make_host_batch(SMALL, 5)
+    hb.q_codes[:] = 0
+    o, lse = run_fp8_extend(hb)
+    ro, rlse = oracle_fp8_extend(hb)
+    assert rel_l2(o, ro) <= 1e-2
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-4)
+
+
+def test_fp8_extend_with_one_new_token_equals_fp8_decode():
+    """Same inputs through both 8-bit kernels: n = 1 per request in the extend,
+    one decode row per request (sfQ per row = per request)."""
+    torch = torch_mod()
+    pkv = _pkv()
+    spec = Spec("f8_ext_n1", "extend", 6, 32, 8, 128, 16, (0, 900), 1, dtype="fp8", k_block=16)
+    hb = make_host_batch(spec, 6)
+    lay = hb.layout
+    o_ext, l_ext = run_fp8_extend(hb)
+    k_pool = dev_u8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F))
+    v_pool = dev_u8(pool_before_store(hb.v_codes, lay.new_slots, fill=0x7F))
+    params = pkv.Params(32, 8, 128, 16, max_kv_len=lay.req_to_token.shape[1], kv_dtype=pkv.PKV_FP8_E4M3,
+                        q_block=1, k_block=16)
+    seq, rtt = dev_i32(lay.seq_lens), dev_i32(lay.req_to_token)
+    plan = pkv.plan_metadata(params, pkv.PKV_DECODE, seq)
+    pkv.kv_store(params, k_pool, v_pool, dev_u8(hb.k_new_codes), dev_u8(hb.v_new_codes), dev_i32(lay.new_slots))
+    lse = torch.empty((spec.batch, 32), dtype=torch.float32, device="cuda")
+    out = pkv.attn_decode(params, dev_u8(hb.q_codes), k_pool, v_pool, rtt, seq, plan, lse=lse, sfq=dev_f32(hb.sfq),
+                          sfk=dev_f32(hb.sfk), sfv=dev_f32(hb.sfv))
+    torch.cuda.synchronize()
+    o_dec = host(out)
+    assert rel_l2(o_ext, o_dec) <= FP8_REL_L2
+    assert np.abs(l_ext - lse.cpu().numpy()).max() <= 1e-3
