@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode KV-read GB/s (% of HBM peak); extend TFLOP/s (% of MFMA peak)"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "flashattention_paged_kv_amd", "csrc")
 
@@ -50,7 +51,8 @@ KERNEL_SOURCES = {
     "decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "long_decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "decode_fp8": ["decode_fp8.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
-    "extend_bf16": ["extend_bf16.hip", "plan.hip", "device_common.h"],
+    "extend_bf16": ["extend_bf16.hip", "lds_dma.h", "plan.hip", "device_common.h"],
+    "extend_fp8": ["extend_fp8.hip", "lds_dma.h", "plan.hip", "device_common.h"],
 }
 
 
@@ -82,6 +84,7 @@ CALL_KERNELS = {
     "decode_fp8": ("decode_fp8_kernel", "decode_merge_kernel"),
     "decode_n4_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
     "extend_bf16": ("extend_bf16_kernel",),
+    "extend_fp8": ("extend_fp8_kernel",),
 }
 COPY_BYTES = 1 << 30
 
@@ -247,11 +250,13 @@ class ExtendRunner:
         self.torch, self.pkv = torch, pkv
         spec = workloads.SPECS[name]
         self.spec = spec
+        self.fp8 = spec.dtype == "fp8"
         self.db = workloads.make_device_batch(spec, seed=0, layers=layers)
         lay = self.db.layout
         self.layers = layers
+        kw = dict(kv_dtype=pkv.PKV_FP8_E4M3, q_block=1, k_block=spec.k_block) if self.fp8 else {}
         self.params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
-                                 max_kv_len=lay.req_to_token.shape[1])
+                                 max_kv_len=lay.req_to_token.shape[1], **kw)
         self.total_q = lay.total_q
         ws_bytes, _ = pkv.workspace_size(self.params, pkv.PKV_EXTEND, spec.batch, self.total_q)
         self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
@@ -277,28 +282,31 @@ class ExtendRunner:
         pkv, db = self.pkv, self.db
         for l in range(self.layers):
             pkv.attn_extend(self.params, db.q, db.k_pools[l], db.v_pools[l], db.req_to_token, db.seq_lens,
-                            db.cu_seqlens_q, self.plan, out=self.out[l], lse=self.lse)
+                            db.cu_seqlens_q, self.plan, out=self.out[l], lse=self.lse,
+                            sfq=db.sfq, sfk=db.sfk, sfv=db.sfv)
 
     def describe(self):
         s = self.spec
         return {"workload": s.name, "batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
                 "head_dim": s.head_dim, "page_size": s.page_size, "prefix_len": f"U{list(s.prefix)}",
                 "new_len": f"U{list(s.new)}", "total_q": self.total_q, "layers_per_step": self.layers,
-                "flops_per_layer": self.flops_per_layer}
+                "kv_dtype": "fp8_e4m3" if self.fp8 else "bf16", "flops_per_layer": self.flops_per_layer}
 
     def roofline(self, avg_launch_s, workload):
         achieved = self.flops_per_layer / avg_launch_s / 1e12
-        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_counters(workload),
-                "kernel": "extend_bf16_kernel", "algorithmic_flops_per_launch": self.flops_per_layer,
-                "avg_launch_us": round(avg_launch_s * 1e6, 2)}
+        peak = PEAK_FP8_TFLOPS if self.fp8 else PEAK_BF16_TFLOPS  # the contraction's own dtype
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic_from_counters(workload),
+                "kernel": "extend_fp8_kernel" if self.fp8 else "extend_bf16_kernel",
+                "algorithmic_flops_per_launch": self.flops_per_layer, "avg_launch_us": round(avg_launch_s * 1e6, 2)}
 
 
 RUNNERS = {"decode_bf16": DecodeRunner, "long_decode_bf16": DecodeRunner, "decode_fp8": DecodeRunner,
-           "decode_n4_bf16": DecodeRunner, "extend_bf16": ExtendRunner}
+           "decode_n4_bf16": DecodeRunner, "extend_bf16": ExtendRunner, "extend_fp8": ExtendRunner}
 UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "decode_fp8": "GB/s", "decode_n4_bf16": "GB/s",
-         "extend_bf16": "TFLOP/s"}
-DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "decode_fp8": 4, "decode_n4_bf16": 4, "extend_bf16": 4}
+         "extend_bf16": "TFLOP/s", "extend_fp8": "TFLOP/s"}
+DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "decode_fp8": 4, "decode_n4_bf16": 4, "extend_bf16": 4,
+                  "extend_fp8": 4}
 
 
 def capture(runner, torch):
@@ -361,7 +369,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_bf16", choices=sorted(RUNNERS))
     ap.add_argument("--layers", type=int, default=0, help="layers (distinct K/V pools) per step")
-    ap.add_argument("--secondary", default="extend_bf16,long_decode_bf16,decode_fp8,decode_n4_bf16",
+    ap.add_argument("--secondary", default="extend_bf16,long_decode_bf16,decode_fp8,decode_n4_bf16,extend_fp8",
                     help="comma list of workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -112,3 +112,47 @@ def test_fp8_extend_with_one_new_token_equals_fp8_decode():
     o_dec = host(out)
     assert rel_l2(o_ext, o_dec) <= FP8_REL_L2
     assert np.abs(l_ext - lse.cpu().numpy()).max() <= 1e-3
+
+
+def test_full_size_fp8_extend_sampled():
+    """The full 8-bit extend workload in the bench's launch configuration;
+    sampled (row, head) pairs are recomputed by the oracle over their visible keys."""
+    torch = torch_mod()
+    pkv = _pkv()
+    from workloads import SPECS, make_device_batch
+    spec = SPECS["extend_fp8"]
+    db = make_device_batch(spec, seed=0, layers=1)
+    lay = db.layout
+    params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                        max_kv_len=lay.req_to_token.shape[1], kv_dtype=pkv.PKV_FP8_E4M3, q_block=1,
+                        k_block=spec.k_block)
+    plan = pkv.plan_metadata(params, pkv.PKV_EXTEND, db.seq_lens, db.cu_seqlens_q, total_q=lay.total_q)
+    pkv.kv_store(params, db.k_pools[0], db.v_pools[0], db.k_new[0], db.v_new[0], db.new_slots)
+    lse = torch.empty((lay.total_q, spec.num_q_heads), dtype=torch.float32, device="cuda")
+    out = pkv.attn_extend(params, db.q, db.k_pools[0], db.v_pools[0], db.req_to_token, db.seq_lens,
+                          db.cu_seqlens_q, plan, lse=lse, sfq=db.sfq, sfk=db.sfk, sfv=db.sfv)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    sfq, sfk, sfv = db.sfq.cpu().numpy(), db.sfk.cpu().numpy(), db.sfv.cpu().numpy()
+    rng = np.random.default_rng(1)
+    G = spec.num_q_heads // spec.num_kv_heads
+    got, want = [], []
+    for _ in range(40):
+        b = int(rng.integers(0, spec.batch))
+        n, p = int(lay.new_lens[b]), int(lay.prefix_lens[b])
+        i = int(rng.choice([0, n - 1, int(rng.integers(0, n))]))
+        h = int(rng.integers(0, spec.num_q_heads))
+        g = h // G
+        row = int(lay.cu_seqlens_q[b]) + i
+        vis = p + i + 1
+        slots = db.req_to_token[b, :vis].long()
+        K = db.k_pools[0][slots, g:g + 1].cpu().numpy()
+        V = db.v_pools[0][slots, g:g + 1].cpu().numpy()
+        q8 = db.q[row:row + 1, h:h + 1].cpu().numpy()
+        # one decode-shaped request over the row's visible keys (Hq = Hkv = 1)
+        ro, rl = oracle.sage_decode(q8, K, V, np.arange(vis)[None], [vis], sfq[row:row + 1, h:h + 1],
+                                    sfk[b:b + 1, g:g + 1], sfv[b:b + 1, g:g + 1], spec.k_block)
+        got.append(host(out[row:row + 1, h:h + 1]).ravel())
+        want.append(ro.ravel())
+        assert abs(float(lse[row, h]) - rl[0, 0]) <= 1e-3
+    assert rel_l2(np.concatenate(got), np.concatenate(want)) <= FP8_REL_L2

@@ -24,6 +24,9 @@ name                   description
                        per-(b,h) sfQ and per-channel sfV drawn from U[0.5,2]
 ``decode_n4_bf16``     as ``decode_bf16`` with 4 new tokens per request
                        checked in one decode call (a verify step)
+``extend_fp8``         as ``extend_bf16`` with E4M3 K/V, sfQ per new-token
+                       row, sfK per 16 keys (the Sage page's default blocks),
+                       per-channel sfV
 =====================  =====================================================
 
 Decode workloads append n new tokens per request (one unless stated): the
@@ -78,12 +81,14 @@ SPECS = {
     "long_decode_bf16": Spec("long_decode_bf16", "decode", 8, 64, 8, 128, 64,
                              (32768, 131072), 1),
     "decode_n4_bf16": Spec("decode_n4_bf16", "decode", 64, 32, 8, 128, 16, (512, 4096), 4),
+    "extend_fp8": Spec("extend_fp8", "extend", 16, 32, 8, 128, 16, (0, 2048), (128, 2048), dtype="fp8",
+                       k_block=16, q_block=1),
     "decode_fp8": Spec("decode_fp8", "decode", 64, 32, 8, 128, 16, (1024, 8192), 1,
                        dtype="fp8", k_block=64, q_block=1),
 }
 
 # Index used to derive the seed of each named workload (1000 + index).
-SPEC_INDEX = {"tiny_decode": 1, "tiny_extend": 1, "decode_bf16": 2, "extend_bf16": 3, "decode_n4_bf16": 6,
+SPEC_INDEX = {"tiny_decode": 1, "tiny_extend": 1, "decode_bf16": 2, "extend_bf16": 3, "decode_n4_bf16": 6, "extend_fp8": 7,
               "long_decode_bf16": 4, "decode_fp8": 5}
 
 
