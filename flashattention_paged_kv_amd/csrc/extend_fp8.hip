@@ -14,8 +14,10 @@
 //  * Sᵀ = K8·Q8ᵀ: K rows from LDS are the A operand (32 bytes per lane),
 //    the wave's Q8 rows the B operand (registers); each lane gets one row
 //    and 16 keys of every 32-key block, as in the bf16 kernel.  The Q and K
-//    scales multiply the fp32 scores before the row max (sfK per 16-key
-//    sub-block, staged in LDS with the slot indices).
+//    scales (positive, as quantisation scales are) enter before the row max:
+//    per 16-key sub-block (sfK staged in LDS with the slot indices) the max
+//    raw score times the sub-block's factor, and fma(raw, factor, -m) in the
+//    exponent.
 //  * The running max is exact (no slack), so 448·p never exceeds 448 and
 //    P8 is a plain E4M3 conversion of fp32 448·p.
 //  * Oᵀ += V8ᵀ·P8ᵀ: the contraction runs over the 64 keys in the order each
@@ -42,6 +44,7 @@ constexpr int kWaves8 = kExtendRows / 32;
 constexpr int kThreads8 = 64 * kWaves8;
 constexpr int kStages8 = 2;
 constexpr int kSlotStages8 = 3;
+constexpr float kLog2_448 = 8.807354922057604f;
 
 struct Smem8 {
   static constexpr int RB = D8;                        // bytes per key row
@@ -258,18 +261,30 @@ __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2))) 
       }
       if (kb == 0) mid();
     }
-    // scores in log2 units: raw · sm_scale·log2(e)·sfQ · sfK of the key's 16-key sub-block
+    // scores in log2 units are raw · f_sb, f_sb = sm_scale·log2(e)·sfQ·sfK of
+    // the key's 16-key sub-block sb; with positive scales the row max is the
+    // largest of (max raw score of sb) · f_sb, and the exponentials take
+    // fma(raw, f_sb, -m) below, so no score is scaled on its own
+    float f[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) f[sb] = rowc * sfk4[sb];
+    if (masked) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) <= pos - t0h - 4 * jh ? s[kb][r] : kNegInf;
+    }
     float mx = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float f = rowc * sfk4[2 * kb + (r >> 3)];
-        float v = s[kb][r] * f;
-        if (masked) v = 32 * kb + 8 * (r >> 2) + (r & 3) <= pos - t0h - 4 * jh ? v : kNegInf;
-        s[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
+    for (int sb = 0; sb < 4; ++sb) {
+      const int kb = sb >> 1, r0 = 8 * (sb & 1);
+      float m3 = fmaxf(fmaxf(s[kb][r0], s[kb][r0 + 1]), s[kb][r0 + 2]);
+      m3 = fmaxf(fmaxf(m3, s[kb][r0 + 3]), s[kb][r0 + 4]);
+      m3 = fmaxf(fmaxf(m3, s[kb][r0 + 5]), s[kb][r0 + 6]);
+      m3 = fmaxf(m3, s[kb][r0 + 7]);
+      mx = fmaxf(mx, m3 * f[sb]);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // exact running max: 448·p <= 448 for every quantised probability
     if (__any(mx > rs.m)) {
@@ -280,7 +295,9 @@ __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2))) 
       for (int db = 0; db < D8 / 32; ++db) rs.acc[db] *= alpha;
       rs.m = m_new;
     }
-    const float mu = rs.m == kNegInf ? 0.f : rs.m;
+    // 448·p = exp2(s - m + log2 448): the quantised probability's factor rides
+    // in the exponent, so P8 is a plain conversion and l sums 448·p
+    const float mu = (rs.m == kNegInf ? 0.f : rs.m) - kLog2_448;
     // P8ᵀ operand: dword 4 kb + q holds keys 32 kb + 8 q + 4 jh + 0..3
     i32x8 pop;
 #pragma unroll
@@ -289,9 +306,9 @@ __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2))) 
       for (int q = 0; q < 4; ++q) {
         float pv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = exp2_fast(s[kb][4 * q + e] - mu);
+        for (int e = 0; e < 4; ++e) pv[e] = exp2_fast(__builtin_fmaf(s[kb][4 * q + e], f[2 * kb + (q >> 1)], -mu));
         rs.lpart += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-        pop[4 * kb + q] = (int)pack_fp8x4(448.f * pv[0], 448.f * pv[1], 448.f * pv[2], 448.f * pv[3]);
+        pop[4 * kb + q] = (int)pack_fp8x4(pv[0], pv[1], pv[2], pv[3]);
       }
     // Oᵀ += V8ᵀ·P8ᵀ: V8ᵀ dwords (2 rd, 2 rd + 1) come from transposing read rd
     // over keys 32 (rd / 2) + 16 (rd % 2) .. +16 (8-key groups 2 rd, 2 rd + 1)
@@ -345,9 +362,9 @@ __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2))) 
   wait_vmem<0>();
 
   // epilogue: Oᵀ[d][row] -> out[token][h][d], with sfV, 1/(448 l) and v_mean
-  const float l = rs.lpart + __shfl_xor(rs.lpart, 32);
+  const float l = rs.lpart + __shfl_xor(rs.lpart, 32);  // 448 · Σ p
   if (!row_ok) return;
-  const float inv = l > 0.f ? 1.f / (448.f * l) : 0.f;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   const float* sfv = a.sfv + ((int64_t)b * a.hkv + g) * D8;
   const float* vmean = a.v_mean ? a.v_mean + ((int64_t)b * a.hkv + g) * D8 : nullptr;
   uint16_t* orow = static_cast<uint16_t*>(a.out) + ((q0 + ti) * a.hq + h) * (int64_t)D8;
@@ -364,7 +381,7 @@ __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2))) 
       w[1] = pack_bf16x2(o[2], o[3]);
       *reinterpret_cast<u32x2*>(orow + d0) = w;
     }
-  if (jh == 0 && a.lse) a.lse[(q0 + ti) * a.hq + h] = l > 0.f ? (rs.m + __log2f(l)) * kLn2 : kNegInf;
+  if (jh == 0 && a.lse) a.lse[(q0 + ti) * a.hq + h] = l > 0.f ? (rs.m + __log2f(l) - kLog2_448) * kLn2 : kNegInf;
 }
 
 hipError_t launch_extend_fp8(const ExtendArgs& a, int64_t capacity, hipStream_t s) {

@@ -160,8 +160,9 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
  * path (kv_dtype == PKV_FP8_E4M3, q_block == 1): q and pools hold E4M3 bytes
  * and the Sage formula of pkv_attn_decode applies to every row, with sfq
  * float [total_q, Hq] (one scale per row), sfk [B, Hkv, ceil(max_kv_len /
- * k_block)], sfv and v_mean [B, Hkv, d] (v_mean may be NULL); the running
- * maximum is exact, so no quantised probability exceeds 448.  `workspace`
+ * k_block)], sfv and v_mean [B, Hkv, d] (v_mean may be NULL); sfq and sfk
+ * must be positive (as quantisation scales are; values are not checked); the
+ * running maximum is exact, so no quantised probability exceeds 448.  `workspace`
  * comes from pkv_plan_metadata(PKV_EXTEND) with the same batch and total_q.
  * `scratch` is not used (may be NULL). */
 int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void* q,
