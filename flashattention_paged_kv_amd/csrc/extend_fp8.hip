@@ -7,10 +7,11 @@
 //
 // One sfQ per row (the page's default q_block = 1).  The structure is the
 // bf16 extend's (work item = request, query tile, kv head; 256 rows as 8
-// waves x 32 rows; 128-key tiles staged through LDS by direct global -> LDS
+// waves x 32 rows; key tiles staged through LDS by direct global -> LDS
 // loads, 2-stage ring; causal mask bottom-right aligned), with 8-bit tiles
-// (128 bytes per row, half the LDS) and the gfx950 fp8 MFMA 32x32x64
-// (f8f6f4, unit block scales):
+// (128 bytes per row) and the gfx950 fp8 MFMA 32x32x64
+// (f8f6f4, unit block scales); 8-bit rows let a 2-stage ring hold 256-key
+// tiles, computed in four 64-key parts:
 //  * Sᵀ = K8·Q8ᵀ: K rows from LDS are the A operand (32 bytes per lane),
 //    the wave's Q8 rows the B operand (registers); each lane gets one row
 //    and 16 keys of every 32-key block, as in the bf16 kernel.  The Q and K
@@ -38,8 +39,9 @@ namespace pkv {
 namespace {
 
 constexpr int D8 = 128;                 // head_dim (bytes per 8-bit row)
-constexpr int kBN8 = 128;               // keys per tile, computed in two 64-key halves
+constexpr int kBN8 = 256;               // keys per tile, computed in four 64-key parts
 constexpr int kHalf8 = 64;
+constexpr int kParts8 = kBN8 / kHalf8;
 constexpr int kWaves8 = kExtendRows / 32;
 constexpr int kThreads8 = 64 * kWaves8;
 constexpr int kStages8 = 2;
@@ -48,12 +50,12 @@ constexpr float kLog2_448 = 8.807354922057604f;
 
 struct Smem8 {
   static constexpr int RB = D8;                        // bytes per key row
-  static constexpr int MAT = kBN8 * RB;                // one matrix tile (16 KB)
+  static constexpr int MAT = kBN8 * RB;                // one matrix tile (32 KB)
   static constexpr int VOFF = kStages8 * MAT;          // V tiles follow the K tiles
   static constexpr int ROWS_PER_KB = 1024 / RB;        // rows written by one 64-lane 16-byte load (8)
-  static constexpr int NQ = kBN8 / ROWS_PER_KB / kWaves8;  // such loads per wave and matrix (2)
+  static constexpr int NQ = kBN8 / ROWS_PER_KB / kWaves8;  // such loads per wave and matrix (4)
   static constexpr int SLOT_BYTES = kBN8 * 4;          // req_to_token entries of a tile
-  static constexpr int SFK_BYTES = 256;                // sfK of the tile's 16-key sub-blocks (8 used)
+  static constexpr int SFK_BYTES = 256;                // sfK of the tile's 16-key sub-blocks (16 used)
   static constexpr int SLOT0 = 2 * kStages8 * MAT;
   static constexpr int SFK0 = SLOT0 + kSlotStages8 * SLOT_BYTES;
   static constexpr int TOTAL = SFK0 + kSlotStages8 * SFK_BYTES;
@@ -107,14 +109,14 @@ __device__ __forceinline__ void issue_rows8(const int (&sv)[Smem8::NQ], char* st
   }
 }
 
-// req_to_token entries of a tile's 128 keys and the sfK of its eight 16-key
+// req_to_token entries of a tile's 256 keys and the sfK of its sixteen 16-key
 // sub-blocks (one wave; positions past kv_end read the last valid entry).
 __device__ __forceinline__ void issue_slots8(const int32_t* __restrict__ rtt_row, const float* __restrict__ sfk_row,
                                              int k_block, int t0, int kv_end, char* slot_stage, char* sfk_stage,
                                              int lane) {
-  dma4(rtt_row + min(t0 + lane, kv_end - 1), lds_addr(slot_stage));
-  dma4(rtt_row + min(t0 + 64 + lane, kv_end - 1), lds_addr(slot_stage) + 256);
-  dma4(sfk_row + min(t0 + 16 * (lane & 7), kv_end - 1) / k_block, lds_addr(sfk_stage));
+#pragma unroll
+  for (int c = 0; c < kBN8 / 64; ++c) dma4(rtt_row + min(t0 + 64 * c + lane, kv_end - 1), lds_addr(slot_stage) + 256 * c);
+  dma4(sfk_row + min(t0 + 16 * (lane & 15), kv_end - 1) / k_block, lds_addr(sfk_stage));
 }
 
 __device__ __forceinline__ void zero_rows_past_end8(char* stage, int t0, int kv_end, int wave, int lane) {
@@ -334,9 +336,15 @@ __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2))) 
     const bool kv1 = tile + 1 < ntiles;
     int sv[S::NQ];
     if (kv1) read_slots8(slot_stage(tile + 1), wave, lane, sv);
-    const floatx4 sfk_lo = *reinterpret_cast<const floatx4*>(sfk_stage(tile));
-    const floatx4 sfk_hi = *reinterpret_cast<const floatx4*>(sfk_stage(tile) + 16);
-    const float sk[8] = {sfk_lo[0], sfk_lo[1], sfk_lo[2], sfk_lo[3], sfk_hi[0], sfk_hi[1], sfk_hi[2], sfk_hi[3]};
+    float sk[4 * kParts8];
+#pragma unroll
+    for (int c = 0; c < kParts8; ++c) {
+      const floatx4 f4 = *reinterpret_cast<const floatx4*>(sfk_stage(tile) + 16 * c);
+      sk[4 * c] = f4[0];
+      sk[4 * c + 1] = f4[1];
+      sk[4 * c + 2] = f4[2];
+      sk[4 * c + 3] = f4[3];
+    }
     auto loads = [&]() __attribute__((always_inline)) {
       if (sl2)
         issue_slots8(rtt_row, sfk_row, a.k_block, t0 + 2 * kBN8, kv_end, slot_stage(tile + 2), sfk_stage(tile + 2),
@@ -346,8 +354,13 @@ __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2))) 
     const char* kt = kv0 + J * S::MAT;
     if (t0 <= wave_max_pos) {
       half(kt, kt, sk, t0, t0 + kHalf8 - 1 > wave_min_pos, loads);
-      if (t0 + kHalf8 <= wave_max_pos)
-        half(kt + kHalf8 * S::RB, kt + kHalf8 * S::RB, sk + 4, t0 + kHalf8, t0 + kBN8 - 1 > wave_min_pos, nothing);
+#pragma unroll
+      for (int c = 1; c < kParts8; ++c) {
+        const int tc = t0 + kHalf8 * c;
+        if (tc > wave_max_pos) break;  // causally invisible to every row of the wave
+        half(kt + kHalf8 * c * S::RB, kt + kHalf8 * c * S::RB, sk + 4 * c, tc, tc + kHalf8 - 1 > wave_min_pos,
+             nothing);
+      }
     } else {
       loads();
     }
