@@ -252,7 +252,7 @@ __device__ __forceinline__ void qk_tile(RowState<D>& rs, u32x4 (&pop)[4], const 
     mx1 = fmaxf(fmaxf(mx1, s[1][r]), s[1][r + 1]);
   }
   float mx = fmaxf(fmaxf(mx0, s[0][15]), fmaxf(mx1, s[1][15]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+  mx = max_xor32(mx) * c;
   // lazy rescale: the reference max moves only when a row's max exceeds it by
   // more than 8 (log2 units), so exp2(s - m) <= 256 while acc and l keep
   // referring to the same m

@@ -19,8 +19,10 @@
 //    per 16-key sub-block (sfK staged in LDS with the slot indices) the max
 //    raw score times the sub-block's factor, and fma(raw, factor, -m) in the
 //    exponent.
-//  * The running max is exact (no slack), so 448·p never exceeds 448 and
-//    P8 is a plain E4M3 conversion of fp32 448·p.
+//  * The reference max m is never below a score already seen, so 448·p never
+//    exceeds 448 and P8 is a plain E4M3 conversion of fp32 448·p (the 448
+//    rides in the exponent).  When a row's max passes m, m moves to that max
+//    plus a power-of-two headroom, so later small rises skip the rescale.
 //  * Oᵀ += V8ᵀ·P8ᵀ: the contraction runs over the 64 keys in the order each
 //    lane holds its probabilities, (32-key block, 8-key group, 4 keys); the
 //    V8ᵀ operands are gathered in that same order by 8-bit transposing LDS
@@ -47,6 +49,7 @@ constexpr int kThreads8 = 64 * kWaves8;
 constexpr int kStages8 = 2;
 constexpr int kSlotStages8 = 3;
 constexpr float kLog2_448 = 8.807354922057604f;
+constexpr float kHeadroom8 = 2.f;  // log2 units above a new row max
 
 struct Smem8 {
   static constexpr int RB = D8;                        // bytes per key row
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2))) 
   }
   __syncthreads();
 
-  // one 64-key half: scores, scales, mask, exact running max, P8, PV
+  // one 64-key part: scores, scales, mask, reference max, P8, PV
   auto half = [&](const char* kt, const char* st, const float* sfk4, int t0h, bool masked, auto&& mid)
       __attribute__((always_inline)) {
     floatx16 s[2];
@@ -287,10 +290,13 @@ __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2))) 
       m3 = fmaxf(m3, s[kb][r0 + 7]);
       mx = fmaxf(mx, m3 * f[sb]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // exact running max: 448·p <= 448 for every quantised probability
+    mx = max_xor32(mx);
+    // reference max with headroom: when a row's max passes it, it moves to
+    // that max plus kHeadroom8, so most tiles skip the rescale; every score
+    // stays at or below it, so 448·p <= 448 for every quantised probability
+    // (the power-of-two headroom only shifts the codes' exponents)
     if (__any(mx > rs.m)) {
-      const float m_new = fmaxf(rs.m, mx);
+      const float m_new = mx > rs.m ? mx + kHeadroom8 : rs.m;
       const float alpha = m_new == kNegInf ? 1.f : exp2_fast(rs.m - m_new);
       rs.lpart *= alpha;
 #pragma unroll
