@@ -89,8 +89,7 @@ __device__ __forceinline__ void compute_tile(const KVTile<D>& t, const u32x4 (&q
     sc[4 + r] = (t0 + 16 + 4 * j + r < kv_end) ? s1[r] * scale_log2 : kNegInf;
   }
   float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_xor32(max_xor16(mx));
   // -inf only for a column that has seen no key yet (a new token whose causal
   // limit lies below this tile); it then keeps zero weight
   const float m_new = fmaxf(m, mx);

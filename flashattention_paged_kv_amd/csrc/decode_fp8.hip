@@ -222,8 +222,7 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
     float mx = sc[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m, mx);  // finite: key t0 is in range
     const float alpha = exp2_fast(m - m_new);
     m = m_new;
