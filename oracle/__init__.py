@@ -43,6 +43,14 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
   order; bounds on tile multiples; capacity; the chunk is the smallest that
   meets the item target; longest-first order when items overflow it).
 * ``kv_store``: pinned by a round trip.
+* ``block_sparse_decode`` / ``block_sparse_sage_decode``: pinned by
+  reductions to pinned functions (every block listed equals
+  ``paged_attention`` / ``sage_decode``; equal to them on a page table cut
+  down by hand to the listed positions, with sfK of the logical blocks), the
+  log-sum-exp merge identity over a disjoint split of the listed blocks, and
+  one-hot scores inside and outside the mask.  The mask format and "exact"
+  semantics are a reading (the pages give only densities); the 8-bit
+  running-max caveat of ``sage_decode`` applies.
 """
 from .attention import paged_attention
 from .merge import lse_merge
@@ -51,10 +59,11 @@ from .sage import sage_decode, sage_extend
 from .plan import plan_decode, plan_extend, decode_target_items, DECODE_TILE, EXTEND_BLOCK_M
 from .kv_store import kv_store
 from .memory import score_matrix_bytes
+from .block_sparse import block_sparse_decode, block_sparse_sage_decode
 
 __all__ = [
     "paged_attention", "lse_merge", "e4m3_encode",
     "e4m3_decode", "E4M3_MAX", "sage_decode", "sage_extend", "plan_decode", "plan_extend",
     "DECODE_TILE", "EXTEND_BLOCK_M", "decode_target_items", "kv_store",
-    "score_matrix_bytes",
+    "score_matrix_bytes", "block_sparse_decode", "block_sparse_sage_decode",
 ]

@@ -69,6 +69,8 @@ class Spec:
     k_block: int = 64  # fp8: tokens per sfK block
     q_block: int = 1  # fp8: q rows per sfQ block
     scale_range: Tuple[float, float] = (0.5, 2.0)
+    sparse_block: int = 0  # block-sparse decode: logical positions per KV block (0 = dense)
+    density: float = 0.0  # block-sparse decode: share of each request's blocks selected
 
 
 SPECS = {
@@ -85,11 +87,15 @@ SPECS = {
                        k_block=16, q_block=1),
     "decode_fp8": Spec("decode_fp8", "decode", 64, 32, 8, 128, 16, (1024, 8192), 1,
                        dtype="fp8", k_block=64, q_block=1),
+    "sparse_decode_bf16": Spec("sparse_decode_bf16", "decode", 8, 40, 40, 128, 16, (15360, 75600), 1,
+                               sparse_block=64, density=0.10),
+    "sparse_decode_fp8": Spec("sparse_decode_fp8", "decode", 8, 40, 40, 128, 16, (15360, 75600), 1,
+                              dtype="fp8", k_block=64, q_block=1, sparse_block=64, density=0.10),
 }
 
 # Index used to derive the seed of each named workload (1000 + index).
 SPEC_INDEX = {"tiny_decode": 1, "tiny_extend": 1, "decode_bf16": 2, "extend_bf16": 3, "decode_n4_bf16": 6, "extend_fp8": 7,
-              "long_decode_bf16": 4, "decode_fp8": 5}
+              "long_decode_bf16": 4, "decode_fp8": 5, "sparse_decode_bf16": 8, "sparse_decode_fp8": 10}
 
 
 def seed_sequence(spec: Spec, seed: int) -> list:
@@ -111,6 +117,8 @@ class Layout:
     new_slots: np.ndarray  # int32 [T] slot of each new token, request-major
     slot_owner: np.ndarray  # int32 [pool_slots] request owning a slot, -1 if free
     slot_pos: np.ndarray  # int32 [pool_slots] position of a slot in its request
+    blk_indptr: Optional[np.ndarray] = None  # block-sparse decode: int32 [B+1]
+    blk_indices: Optional[np.ndarray] = None  # int32 [nnz], ascending per request
 
     @property
     def total_q(self) -> int:
@@ -130,6 +138,25 @@ def _draw(rng: np.random.Generator, spec_val: LenSpec, batch: int) -> np.ndarray
     arr = np.asarray(spec_val, dtype=np.int64)
     assert arr.shape == (batch,), (arr.shape, batch)
     return arr
+
+
+def block_mask(seq_lens, block_size: int, density: float, rng: np.random.Generator):
+    """Selected KV blocks per request (CSR): ceil(density · n) of the n =
+    ceil(L / block_size) blocks, at least one; the newest block (holding the
+    decoded token) is always kept, the others are drawn uniformly without
+    replacement; ascending per request."""
+    indptr = [0]
+    indices = []
+    for L in np.asarray(seq_lens, np.int64):
+        n = int((L + block_size - 1) // block_size)
+        if n == 0:
+            indptr.append(len(indices))
+            continue
+        count = min(n, max(1, int(np.ceil(density * n))))
+        rest = rng.choice(n - 1, size=count - 1, replace=False) if count > 1 else np.zeros(0, np.int64)
+        indices.extend(sorted(int(x) for x in rest) + [n - 1])
+        indptr.append(len(indices))
+    return np.asarray(indptr, np.int32), np.asarray(indices, np.int32)
 
 
 def make_layout(spec: Spec, seed: int = 0, rng: Optional[np.random.Generator] = None,
@@ -184,6 +211,10 @@ def make_layout(spec: Spec, seed: int = 0, rng: Optional[np.random.Generator] = 
                  seq_lens=seq.astype(np.int32), cu_seqlens_q=cu.astype(np.int32),
                  req_to_token=rtt.astype(np.int32), pool_slots=num_pages * P,
                  new_slots=new_slots.astype(np.int32), slot_owner=slot_owner, slot_pos=slot_pos)
+    if spec.sparse_block > 0:
+        # drawn from a stream of its own, so the other draws match the dense layout
+        mrng = np.random.default_rng(seed_sequence(spec, seed) + [77])
+        lay.blk_indptr, lay.blk_indices = block_mask(lay.seq_lens, spec.sparse_block, spec.density, mrng)
     return lay, rng
 
 
@@ -323,6 +354,8 @@ class DeviceBatch:
     new_slots: "object"  # int32 [T]
     sfq: "object" = None
     sfk: "object" = None
+    blk_indptr: "object" = None  # block-sparse decode, int32 [B+1]
+    blk_indices: "object" = None  # int32 [nnz]
     sfv: "object" = None
 
 
@@ -350,6 +383,8 @@ def make_device_batch(spec: Spec, seed: int = 0, device="cuda", layers: int = 1,
     db = DeviceBatch(layout=lay, q=None, k_pools=[], v_pools=[], k_new=[], v_new=[],
                      req_to_token=i32(lay.req_to_token), seq_lens=i32(lay.seq_lens),
                      cu_seqlens_q=i32(lay.cu_seqlens_q), new_slots=new_slots)
+    if lay.blk_indptr is not None:
+        db.blk_indptr, db.blk_indices = i32(lay.blk_indptr), i32(lay.blk_indices)
     if spec.dtype == "fp8":
         B = spec.batch
         lo, hi = spec.scale_range
