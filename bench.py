@@ -53,6 +53,10 @@ KERNEL_SOURCES = {
     "decode_fp8": ["decode_fp8.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "extend_bf16": ["extend_bf16.hip", "lds_dma.h", "plan.hip", "device_common.h"],
     "extend_fp8": ["extend_fp8.hip", "lds_dma.h", "plan.hip", "device_common.h"],
+    "sparse_decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h",
+                           "block_sparse.hip"],
+    "sparse_decode_fp8": ["decode_fp8.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h",
+                          "block_sparse.hip"],
 }
 
 
@@ -85,6 +89,8 @@ CALL_KERNELS = {
     "decode_n4_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
     "extend_bf16": ("extend_bf16_kernel",),
     "extend_fp8": ("extend_fp8_kernel",),
+    "sparse_decode_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
+    "sparse_decode_fp8": ("decode_fp8_kernel", "decode_merge_kernel"),
 }
 COPY_BYTES = 1 << 30
 
@@ -245,6 +251,80 @@ class DecodeRunner:
                           f"the {spec.batch}-request batch), all {spec.num_q_heads} heads, fp64"}
 
 
+class SparseDecodeRunner(DecodeRunner):
+    """Block-sparse decode: once per batch the compacted page table of the
+    listed blocks (and its sfK), then the plan over the selected lengths; the
+    attention calls run on that table.  Work per layer = K+V bytes of the
+    selected keys."""
+
+    def __init__(self, name, layers, torch, pkv, workloads):
+        super().__init__(name, layers, torch, pkv, workloads)
+        lay, spec = self.db.layout, self.spec
+        bs = spec.sparse_block
+        sel = 0
+        for b in range(spec.batch):
+            L = int(lay.seq_lens[b])
+            for k in lay.blk_indices[lay.blk_indptr[b]:lay.blk_indptr[b + 1]]:
+                sel += max(0, min(bs, L - int(k) * bs))
+        self.selected_tokens = sel
+        esize = 1 if self.fp8 else 2
+        self.kv_bytes_per_layer = sel * spec.num_kv_heads * spec.head_dim * 2 * esize
+        self.work_per_step = self.kv_bytes_per_layer * layers
+
+    def pre(self):
+        """The once-per-step work: every layer's K/V store, the sparse tables and the plan."""
+        pkv, db = self.pkv, self.db
+        for l in range(self.layers):
+            pkv.kv_store(self.params, db.k_pools[l], db.v_pools[l], db.k_new[l], db.v_new[l], db.new_slots)
+        self.srtt, self.slens, self.ssfk = pkv.block_sparse_table(
+            self.params, db.seq_lens, db.req_to_token, db.blk_indptr, db.blk_indices, self.spec.sparse_block,
+            sfk=db.sfk)
+        self.plan = pkv.plan_metadata(self.params, pkv.PKV_DECODE, self.slens, workspace=self.ws)
+
+    def attn(self):
+        pkv, db = self.pkv, self.db
+        for l in range(self.layers):
+            pkv.attn_decode(self.params, db.q, db.k_pools[l], db.v_pools[l], self.srtt, self.slens, self.plan,
+                            scratch=self.scratch, out=self.out[l], lse=self.lse,
+                            sfq=db.sfq, sfk=self.ssfk, sfv=db.sfv)
+
+    def describe(self):
+        d = super().describe()
+        d.update({"block_size": self.spec.sparse_block, "density": self.spec.density,
+                  "selected_tokens": self.selected_tokens})
+        return d
+
+    def cpu_baseline(self, budget_s, oracle):
+        """The fp64 block-sparse oracle on layer 0, request by request until the budget is spent."""
+        db, spec = self.db, self.spec
+        lay = db.layout
+        if self.fp8:
+            q, kp, vp = db.q.cpu().numpy(), db.k_pools[0].cpu().numpy(), db.v_pools[0].cpu().numpy()
+            sfq, sfk, sfv = db.sfq.cpu().numpy(), db.sfk.cpu().numpy(), db.sfv.cpu().numpy()
+        else:
+            q, kp, vp = (t.float().cpu().numpy() for t in (db.q, db.k_pools[0], db.v_pools[0]))
+        bs = spec.sparse_block
+        done_bytes, n = 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            b = n % spec.batch
+            blocks = lay.blk_indices[lay.blk_indptr[b]:lay.blk_indptr[b + 1]]
+            ip = [0, len(blocks)]
+            rtt, L = lay.req_to_token[b:b + 1], lay.seq_lens[b:b + 1]
+            if self.fp8:
+                oracle.block_sparse_sage_decode(q[b:b + 1], kp, vp, rtt, L, ip, blocks, bs, sfq[b:b + 1],
+                                                sfk[b:b + 1], sfv[b:b + 1], spec.k_block)
+            else:
+                oracle.block_sparse_decode(q[b:b + 1], kp, vp, rtt, L, ip, blocks, bs)
+            sel = sum(max(0, min(bs, int(L[0]) - int(k) * bs)) for k in blocks)
+            done_bytes += sel * spec.num_kv_heads * spec.head_dim * 2 * (1 if self.fp8 else 2)
+            n += 1
+        dt = time.perf_counter() - t0
+        return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "seconds": round(dt, 2),
+                "sample": f"layer 0 of {spec.name}: {n} request-attentions over the listed blocks, "
+                          f"all {spec.num_q_heads} heads, fp64"}
+
+
 class ExtendRunner:
     def __init__(self, name, layers, torch, pkv, workloads):
         self.torch, self.pkv = torch, pkv
@@ -302,11 +382,12 @@ class ExtendRunner:
 
 
 RUNNERS = {"decode_bf16": DecodeRunner, "long_decode_bf16": DecodeRunner, "decode_fp8": DecodeRunner,
-           "decode_n4_bf16": DecodeRunner, "extend_bf16": ExtendRunner, "extend_fp8": ExtendRunner}
+           "decode_n4_bf16": DecodeRunner, "extend_bf16": ExtendRunner, "extend_fp8": ExtendRunner,
+           "sparse_decode_bf16": SparseDecodeRunner, "sparse_decode_fp8": SparseDecodeRunner}
 UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "decode_fp8": "GB/s", "decode_n4_bf16": "GB/s",
          "extend_bf16": "TFLOP/s", "extend_fp8": "TFLOP/s"}
 DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "decode_fp8": 4, "decode_n4_bf16": 4, "extend_bf16": 4,
-                  "extend_fp8": 4}
+                  "extend_fp8": 4, "sparse_decode_bf16": 2, "sparse_decode_fp8": 2}
 
 
 def capture(runner, torch):
@@ -369,7 +450,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_bf16", choices=sorted(RUNNERS))
     ap.add_argument("--layers", type=int, default=0, help="layers (distinct K/V pools) per step")
-    ap.add_argument("--secondary", default="extend_bf16,long_decode_bf16,decode_fp8,decode_n4_bf16,extend_fp8",
+    ap.add_argument("--secondary", default="extend_bf16,long_decode_bf16,decode_fp8,decode_n4_bf16,extend_fp8,"
+                                           "sparse_decode_bf16,sparse_decode_fp8",
                     help="comma list of workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

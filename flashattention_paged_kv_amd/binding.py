@@ -21,8 +21,8 @@ PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
 PKV_BF16, PKV_FP8_E4M3 = 0, 1
 PKV_DECODE, PKV_EXTEND = 0, 1
 
-EXPORTED = ("pkv_workspace_size", "pkv_plan_metadata", "pkv_kv_store", "pkv_attn_decode",
-            "pkv_attn_extend", "pkv_last_error", "pkv_version")
+EXPORTED = ("pkv_workspace_size", "pkv_plan_metadata", "pkv_kv_store", "pkv_block_sparse_table",
+            "pkv_attn_decode", "pkv_attn_extend", "pkv_last_error", "pkv_version")
 
 
 class PkvError(RuntimeError):
@@ -64,6 +64,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_workspace_size.argtypes = [pp, _I32, _I32, _I64, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
     lib.pkv_plan_metadata.argtypes = [pp, _I32, _I32, _I64, _P, _P, _P, _SZ, _P]
     lib.pkv_kv_store.argtypes = [pp, _P, _P, _I64, _P, _P, _P, _I64, _P]
+    lib.pkv_block_sparse_table.argtypes = [pp, _I32, _P, _P, _I64, _P, _P, _P, _I64, _I32, _P, _P, _P, _P, _P]
     lib.pkv_attn_decode.argtypes = [pp, _P, _P, _P, _P, _P, _I64, _P, _I64, _P, _P, _I32, _F,
                                     _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]
     lib.pkv_attn_extend.argtypes = [pp, _P, _P, _P, _P, _P, _I64, _P, _I64, _P, _P, _P, _I32, _I64,
@@ -152,6 +153,40 @@ def kv_store(params: Params, k_pool, v_pool, k_new, v_new, slots):
     lib = load_library()
     _check(lib.pkv_kv_store(ctypes.byref(params), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0], _ptr(k_new),
                             _ptr(v_new), _ptr(slots), slots.shape[0], _stream()))
+
+
+def block_sparse_table(params: Params, seq_lens, req_to_token, blk_indptr, blk_indices, block_size: int,
+                       req_pool_indices=None, sfk=None):
+    """Compacted page table of a block-sparse decode batch (ascending block
+    lists per request, shared by all heads).  Returns (sparse_req_to_token
+    [B, max_kv_len], sparse_seq_lens [B], sparse_sfk or None); pass them to
+    plan_metadata / attn_decode in place of req_to_token, seq_lens and sfk."""
+    import torch
+    fp8 = params.kv_dtype == PKV_FP8_E4M3
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(req_to_token, "req_to_token", torch.int32, 2)
+    _need(blk_indptr, "blk_indptr", torch.int32, 1)
+    _need(blk_indices, "blk_indices", torch.int32, 1)
+    _need(req_pool_indices, "req_pool_indices", torch.int32, 1)
+    _need(sfk, "sfk", torch.float32)
+    B = seq_lens.shape[0]
+    if blk_indptr.shape[0] != B + 1:
+        raise ValueError("blk_indptr must have batch + 1 entries")
+    dev = seq_lens.device
+    sparse_rtt = torch.empty((B, params.max_kv_len), dtype=torch.int32, device=dev)
+    sparse_lens = torch.empty((B,), dtype=torch.int32, device=dev)
+    sparse_sfk = None
+    if fp8:
+        nblk = -(-params.max_kv_len // params.k_block)
+        if sfk is None or tuple(sfk.shape) != (B, params.num_kv_heads, nblk):
+            raise ValueError(f"sfk must be [B, Hkv, ceil(max_kv_len/k_block)] = {(B, params.num_kv_heads, nblk)}")
+        sparse_sfk = torch.empty_like(sfk)
+    lib = load_library()
+    _check(lib.pkv_block_sparse_table(ctypes.byref(params), B, _ptr(seq_lens), _ptr(req_to_token),
+                                      req_to_token.shape[1], _ptr(req_pool_indices), _ptr(blk_indptr),
+                                      _ptr(blk_indices), blk_indices.shape[0], int(block_size), _ptr(sfk),
+                                      _ptr(sparse_rtt), _ptr(sparse_lens), _ptr(sparse_sfk), _stream()))
+    return sparse_rtt, sparse_lens, sparse_sfk
 
 
 def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan: Plan, scratch=None,

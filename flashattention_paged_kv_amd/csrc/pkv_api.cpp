@@ -182,6 +182,57 @@ int pkv_plan_metadata(const pkv_params* params, int32_t mode, int32_t batch, int
   return check_launch(pkv::launch_plan(a, static_cast<hipStream_t>(stream)), "plan_metadata launch");
 }
 
+int pkv_block_sparse_table(const pkv_params* params, int32_t batch, const int32_t* seq_lens,
+                           const int32_t* req_to_token, int64_t rtt_stride, const int32_t* req_pool_indices,
+                           const int32_t* blk_indptr, const int32_t* blk_indices, int64_t num_indices,
+                           int32_t block_size, const float* sfk, int32_t* sparse_req_to_token,
+                           int32_t* sparse_seq_lens, float* sparse_sfk, void* stream) {
+  if (int rc = check_params(params, PKV_DECODE)) return rc;
+  if (batch < 0) return fail(PKV_EINVAL, "batch=%d must be >= 0", batch);
+  if (params->decode_q_len > 1)
+    return fail(PKV_EUNSUPPORTED, "block-sparse decode takes one new token per request (decode_q_len=%d)",
+                params->decode_q_len);
+  if (!is_pow2(block_size) || block_size > (1 << 20))
+    return fail(PKV_EINVAL, "block_size=%d must be a power of two in [1, 2^20]", block_size);
+  if (num_indices < 0 || num_indices > INT32_MAX)
+    return fail(PKV_EINVAL, "num_indices=%lld must be in [0, 2^31)", (long long)num_indices);
+  if (rtt_stride < params->max_kv_len)
+    return fail(PKV_EINVAL, "rtt_stride=%lld is smaller than max_kv_len=%d", (long long)rtt_stride, params->max_kv_len);
+  const bool fp8 = params->kv_dtype == PKV_FP8_E4M3;
+  if (fp8) {
+    if (block_size % params->k_block != 0)
+      return fail(PKV_EINVAL, "block_size=%d must be a multiple of k_block=%d", block_size, params->k_block);
+    if (batch > 0 && (!sfk || !sparse_sfk)) return fail(PKV_EINVAL, "the fp8_e4m3 path needs sfk and sparse_sfk");
+  } else if (sfk || sparse_sfk) {
+    return fail(PKV_EINVAL, "sfk and sparse_sfk are unsupported by a bf16 plan");
+  }
+  if (batch == 0) return ok();
+  if (!seq_lens || !req_to_token || !blk_indptr || !sparse_req_to_token || !sparse_seq_lens)
+    return fail(PKV_EINVAL, "a required pointer (seq_lens, req_to_token, blk_indptr, sparse outputs) is NULL");
+  if (num_indices > 0 && !blk_indices) return fail(PKV_EINVAL, "blk_indices is NULL");
+  pkv::SparseTableArgs a{};
+  a.seq_lens = seq_lens;
+  a.rtt = req_to_token;
+  a.rpi = req_pool_indices;
+  a.indptr = blk_indptr;
+  a.indices = blk_indices;
+  a.sfk = fp8 ? sfk : nullptr;
+  a.out_rtt = sparse_req_to_token;
+  a.out_lens = sparse_seq_lens;
+  a.out_sfk = fp8 ? sparse_sfk : nullptr;
+  a.rtt_stride = rtt_stride;
+  a.num_indices = num_indices;
+  int shift = 0;
+  while ((1 << shift) < block_size) ++shift;
+  a.block_shift = shift;
+  a.max_kv_len = params->max_kv_len;
+  a.hkv = params->num_kv_heads;
+  a.k_block = fp8 ? params->k_block : 1;
+  a.sfk_stride = fp8 ? (int32_t)pkv::ceil_div(params->max_kv_len, params->k_block) : 0;
+  return check_launch(pkv::launch_block_sparse_table(a, batch, static_cast<hipStream_t>(stream)),
+                      "block_sparse_table launch");
+}
+
 int pkv_kv_store(const pkv_params* params, void* k_pool, void* v_pool, int64_t pool_slots, const void* k_new,
                  const void* v_new, const int32_t* slots, int64_t num_tokens, void* stream) {
   // a plain row copy: the dtype rules of a decode plan cover both pool types

@@ -196,7 +196,24 @@ struct ExtendArgs {
   int32_t k_block, sfk_stride;
 };
 
+// Block-sparse decode: compacted page table of the listed KV blocks.
+constexpr int kSparseSplit = 16;  // workgroups per request
+struct SparseTableArgs {
+  const int32_t* seq_lens;
+  const int32_t* rtt;
+  const int32_t* rpi;
+  const int32_t* indptr;   // [batch + 1]
+  const int32_t* indices;  // [num_indices], ascending per request
+  const float* sfk;        // 8-bit: [batch, hkv, sfk_stride]; else NULL
+  int32_t* out_rtt;        // [batch, max_kv_len]
+  int32_t* out_lens;       // [batch]
+  float* out_sfk;          // 8-bit: [batch, hkv, sfk_stride]; else NULL
+  int64_t rtt_stride, num_indices;
+  int32_t block_shift, max_kv_len, hkv, k_block, sfk_stride;
+};
+
 // ---------------------------------------------------------------- launchers
+hipError_t launch_block_sparse_table(const SparseTableArgs& a, int32_t batch, hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_extend_fp8(const ExtendArgs& a, int64_t capacity, hipStream_t s);
 hipError_t launch_kv_store(void* k_pool, void* v_pool, int64_t pool_slots, const void* k_new,

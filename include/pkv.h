@@ -135,6 +135,34 @@ int pkv_kv_store(const pkv_params* params, void* k_pool, void* v_pool, int64_t p
                  const void* k_new, const void* v_new, const int32_t* slots, int64_t num_tokens,
                  void* stream);
 
+/* Block-sparse DECODE, once per batch (block-sparse mode of the FlashInfer
+ * PrimTS Sage page: README block and the measured cases at densities 0.125
+ * and 0.10).  Request b attends exactly to the keys j < L_b whose block
+ * j / block_size is listed in blk_indices[blk_indptr[b] .. blk_indptr[b+1]),
+ * one list per request shared by all heads; each list must be strictly
+ * ascending (a number outside [0, ceil(L_b / block_size)) selects no key).
+ * This call lays the listed blocks end to end and writes, per request, the
+ * slot of each of those keys in order (sparse_req_to_token, int32
+ * [B, max_kv_len], device, row b = request b), their count V_b
+ * (sparse_seq_lens, int32 [B]) and, on the 8-bit path, the sfK of each
+ * k_block of them (sparse_sfk, float [B, Hkv, ceil(max_kv_len / k_block)];
+ * block_size must be a multiple of k_block; sfk is the full-sequence sfK of
+ * pkv_attn_decode).  One launch; the tables serve every layer.  Block-sparse
+ * attention is then pkv_plan_metadata(PKV_DECODE, seq_lens =
+ * sparse_seq_lens) and pkv_attn_decode(req_to_token = sparse_req_to_token,
+ * rtt_stride = max_kv_len, req_pool_indices = NULL, seq_lens =
+ * sparse_seq_lens, sfk = sparse_sfk): the softmax over a set of keys does
+ * not depend on their order.  block_size: a power of two in [1, 2^20];
+ * decode_q_len must be 1; bf16 plans pass sfk = sparse_sfk = NULL.  A list
+ * that is not ascending gives unspecified numbers but no out-of-bounds
+ * access; empty selections give O = 0 and lse = -inf (v_mean on the 8-bit
+ * path). */
+int pkv_block_sparse_table(const pkv_params* params, int32_t batch, const int32_t* seq_lens,
+                           const int32_t* req_to_token, int64_t rtt_stride, const int32_t* req_pool_indices,
+                           const int32_t* blk_indptr, const int32_t* blk_indices, int64_t num_indices,
+                           int32_t block_size, const float* sfk, int32_t* sparse_req_to_token,
+                           int32_t* sparse_seq_lens, float* sparse_sfk, void* stream);
+
 /* DECODE: one query row per request (q, out: [B, Hq, d]).  bf16 path: q and
  * pools bf16, sfq/sfk/sfv/v_mean must be NULL.  8-bit path (kv_dtype ==
  * PKV_FP8_E4M3): q and pools hold E4M3 bytes and the Sage formula applies:
@@ -162,7 +190,8 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
  * float [total_q, Hq] (one scale per row), sfk [B, Hkv, ceil(max_kv_len /
  * k_block)], sfv and v_mean [B, Hkv, d] (v_mean may be NULL); sfq and sfk
  * must be positive (as quantisation scales are; values are not checked); the
- * running maximum is exact, so no quantised probability exceeds 448.  `workspace`
+ * reference maximum never falls below a score already seen, so no quantised
+ * probability exceeds 448.  `workspace`
  * comes from pkv_plan_metadata(PKV_EXTEND) with the same batch and total_q.
  * `scratch` is not used (may be NULL). */
 int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void* q,

@@ -143,6 +143,23 @@ def test_run_call_argument_errors(lib):
     assert rc == pkv.PKV_OK and pkv.last_error() == ""
 
 
+def test_block_sparse_table_argument_errors(lib):
+    p = pkv.Params(32, 8, 128, 16, 4096)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    call = lambda prm, bs, sfk=None, ssfk=None, nnz=10, stride=4096, batch=4: lib.pkv_block_sparse_table(
+        ctypes.byref(prm), batch, fake, fake, stride, None, fake, fake, nnz, bs, sfk, fake, fake, ssfk, None)
+    assert call(p, 48) == pkv.PKV_EINVAL and "power of two" in pkv.last_error()
+    assert call(p, 64, nnz=-1) == pkv.PKV_EINVAL and "num_indices" in pkv.last_error()
+    assert call(p, 64, stride=100) == pkv.PKV_EINVAL and "rtt_stride" in pkv.last_error()
+    assert call(p, 64, sfk=fake) == pkv.PKV_EINVAL and "unsupported by a bf16 plan" in pkv.last_error()
+    p8 = pkv.Params(32, 8, 128, 16, 4096, kv_dtype=pkv.PKV_FP8_E4M3, q_block=1, k_block=64)
+    assert call(p8, 32, sfk=fake, ssfk=fake) == pkv.PKV_EINVAL and "multiple of k_block" in pkv.last_error()
+    assert call(p8, 64) == pkv.PKV_EINVAL and "needs sfk and sparse_sfk" in pkv.last_error()
+    pn = pkv.Params(32, 8, 128, 16, 4096, decode_q_len=4)
+    assert call(pn, 64) == pkv.PKV_EUNSUPPORTED and "one new token" in pkv.last_error()
+    assert call(p, 64, batch=0) == pkv.PKV_OK and pkv.last_error() == ""
+
+
 def test_workspace_does_not_grow_with_square_of_length(lib):
     """O(N) not O(N^2): the plan workspace and decode scratch at 131072 tokens stay
     far below the materialised score matrix of the FlashAttention memory example."""
