@@ -266,10 +266,13 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int s0, int s1
 template <int D, int WPB>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(DecodeArgs a) {
   const int32_t* __restrict__ ws = a.ws;
-  const int c = (int)blockIdx.x;
+  // 1-D grid, unit group fastest: the workgroups of one chunk are
+  // dispatched back to back and the unused tail of the capacity comes last
+  const int ngroups = (a.hkv * a.head_groups + WPB - 1) / WPB;
+  const int c = __builtin_amdgcn_readfirstlane((int)blockIdx.x / ngroups);  // uniform
   if (c >= ws[WS_NCHUNKS]) return;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
-  const int unit = blockIdx.y * WPB + wv;
+  const int unit = __builtin_amdgcn_readfirstlane(((int)blockIdx.x - c * ngroups) * WPB + wv);
   if (unit >= a.hkv * a.head_groups) return;
   const int tab = ws[WS_CHUNK_TAB];
   const int s0 = tab ? ws[tab + c] : c, s1 = tab ? ws[tab + c + 1] : c + 1;
@@ -292,7 +295,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacit
   // up to 8 waves per workgroup: the kv heads of one split run side by side
   const int units = a.hkv * a.head_groups;
   const int wpb = decode_waves_per_block(units);
-  dim3 grid((unsigned)capacity, (unsigned)ceil_div(units, wpb));
+  dim3 grid((unsigned)(capacity * ceil_div(units, wpb)));
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * wpb), 0, s, a); };
   if (head_dim == 128) {
     if (wpb == 8) go(decode_bf16_kernel<128, 8>); else if (wpb == 4) go(decode_bf16_kernel<128, 4>);

@@ -316,6 +316,10 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
   a.k_block = params->k_block;
   a.sfk_stride = fp8 ? (int32_t)pkv::ceil_div(params->max_kv_len, params->k_block) : 0;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
+  const int64_t units = (int64_t)a.hkv * a.head_groups;
+  if (w.capacity * pkv::ceil_div(units, pkv::decode_waves_per_block((int)units)) > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "decode grid of %lld work items x %lld kv-head units exceeds int32",
+                (long long)w.capacity, (long long)units);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = fp8 ? pkv::launch_decode_fp8(a, params->head_dim, w.capacity, batch, s)
                      : pkv::launch_decode_bf16(a, params->head_dim, w.capacity, batch, s);
