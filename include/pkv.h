@@ -19,9 +19,10 @@
  *   - the scheduling metadata is computed once per batch and reused by every
  *     layer, as in "SGLang의 FA3 디코드 최적화: get_scheduler_metadata 도입"
  *     (intro and code §1-§3);
- *   - the optional 8-bit decode follows the Sage formula of "FlashInfer
- *     PrimTS, Sage Attention 도입으로 8비트 양자화 및 성능 최적화 달성"
- *     (code §1, §4, §5).
+ *   - the optional 8-bit decode and extend follow the Sage formula of
+ *     "FlashInfer PrimTS, Sage Attention 도입으로 8비트 양자화 및 성능 최적화
+ *     달성" (code §1, §4, §5), and the block-sparse decode its block-sparse
+ *     mode (README block and the measured cases).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
