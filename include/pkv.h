@@ -57,7 +57,8 @@
  * its scales): seq_lens are clamped to [0, max_kv_len], query row ranges to
  * [0, total_q], and slots outside [0, pool_slots) are clamped when read and
  * skipped when written, so bad values give wrong numbers but never an
- * out-of-bounds access.
+ * out-of-bounds access.  The one exception is req_pool_indices: the ABI has
+ * no row count for req_to_token, so its values must be valid rows.
  */
 #ifndef PKV_H_
 #define PKV_H_
