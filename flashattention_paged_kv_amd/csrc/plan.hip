@@ -61,6 +61,85 @@ __device__ __forceinline__ int clamp_len(int L, int max_kv_len) {
   return L < 0 ? 0 : (L > max_kv_len ? max_kv_len : L);
 }
 
+__device__ __forceinline__ int wave_inclusive_scan32(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+// Whether the one-wave decode plan below applies (decided on the host too).
+__host__ __device__ __forceinline__ bool plan_decode_by_one_wave(const PlanArgs& a) {
+  return a.mode == PKV_DECODE && a.kv_chunk == 0 && a.batch <= 64 && a.capacity < 2 * (int64_t)kPlanLdsSortMax;
+}
+
+// Balanced decode chunks for at most 64 requests, by one wave (one lane per
+// request, 32-bit scans, no workgroup barrier): the same work list, offsets
+// and chunk table as the workgroup path below.  The chunk table is built in
+// LDS (`tab_lds`, nchunks + 1 <= capacity + 1 entries): every segment lowers
+// its chunk's entry to its own index, so an entry ends as the chunk's first
+// segment (num where no segment was kept).
+__device__ void plan_decode_one_wave(const PlanArgs& a, int32_t* tab_lds) {
+  int32_t* ws = a.ws;
+  int32_t* req = ws + a.req_off;
+  int4* items = reinterpret_cast<int4*>(ws + a.items_off);
+  int32_t* goff = ws + a.tmp_off;  // [B+1] global tile offset of each request
+  int32_t* tab = goff + a.batch + 1;
+  const int B = a.batch, b = threadIdx.x;
+  const bool on = b < B;
+  const int L = on ? clamp_len(a.seq_lens[b], a.max_kv_len) : 0;
+  const int t = on ? (L + a.tile - 1) / a.tile : 0;
+  const int o = wave_inclusive_scan32(t) - t;
+  const int T = __shfl(o + t, 63, 64);
+  const int C = T > a.target_items ? (T + a.target_items - 1) / a.target_items : 1;
+  const int nchunks = T > C ? (T + C - 1) / C : 1;
+  const int nseg = on ? (t == 0 ? 1 : (o + t - 1) / C - o / C + 1) : 0;
+  const int first = wave_inclusive_scan32(nseg) - nseg;
+  const int total = __shfl(first + nseg, 63, 64);
+  const int num = total < a.capacity ? total : (int)a.capacity;
+  if (on) {
+    goff[b] = o;
+    req[b] = first;
+  }
+  if (b == 0) {
+    goff[B] = T;
+    req[B] = total;
+  }
+  for (int cc = b; cc <= nchunks; cc += 64) tab_lds[cc] = num;
+  if (on) {
+    if (t == 0) {  // an empty request keeps one empty segment
+      if (first < num) {
+        items[first] = make_int4(b, 0, 0, -1);
+        atomicMin(&tab_lds[o / C < nchunks ? o / C : nchunks - 1], first);
+      }
+    } else {
+      for (int sgi = 0; sgi < nseg && first + sgi < num; ++sgi) {
+        const int cc = o / C + sgi;
+        const int g0 = o > cc * C ? o : cc * C;
+        const int g1 = o + t < (cc + 1) * C ? o + t : (cc + 1) * C;
+        const int kb = (g0 - o) * a.tile;
+        const int ke = (g1 - o) * a.tile < L ? (g1 - o) * a.tile : L;
+        items[first + sgi] = make_int4(b, kb, ke, nseg > 1 ? first + sgi : -1);
+        atomicMin(&tab_lds[cc], first + sgi);
+      }
+    }
+  }
+  for (int cc = b; cc <= nchunks; cc += 64) tab[cc] = cc == nchunks ? num : tab_lds[cc];
+  if (b == 0) {
+    ws[WS_MODE] = PKV_DECODE;
+    ws[WS_BATCH] = B;
+    ws[WS_NUM_ITEMS] = num;
+    ws[WS_CAPACITY] = (int32_t)a.capacity;
+    ws[WS_CHUNK] = C;
+    ws[WS_TARGET] = a.target_items;
+    ws[WS_NCHUNKS] = nchunks;
+    ws[WS_CHUNK_TAB] = (int32_t)(a.tmp_off + B + 1);
+  }
+}
+
 // Index b with req[b] <= i < req[b+1] (req non-decreasing, req[0] = 0).
 __device__ __forceinline__ int find_request(const int32_t* req, int batch, int64_t i) {
   int lo = 0, hi = batch;  // answer in [lo, hi)
@@ -106,22 +185,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int B = a.batch;
   int64_t carry = 0;
 
+  if (plan_decode_by_one_wave(a)) {  // launched as one wave
+    if (threadIdx.x < 64) plan_decode_one_wave(a, reinterpret_cast<int32_t*>(keys_lds));
+    return;
+  }
   if (a.mode == PKV_DECODE && a.kv_chunk == 0) {
     // Balanced chunks: the requests' tiles (a.tile tokens) laid end to end (request
     // b at global tiles [o_b, o_b + t_b)) are cut into chunks of C tiles,
     // C = ceil(T / target); a chunk is one workgroup and holds the request
     // segments it overlaps, so every workgroup streams the same amount of KV.
-    int32_t* goff = ws + a.tmp_off;  // [B+1] global tile offset of each request
+    // The arrays below are written to the workspace and, when they fit, read
+    // back from copies in LDS (the sort buffer is idle here): each read of
+    // the workspace would be a round trip through L2, and the chunk table's
+    // binary search is a chain of them.
+    int32_t* const lds_i = reinterpret_cast<int32_t*>(keys_lds);
+    const bool in_lds = 2 * ((int64_t)B + 1) + a.capacity <= 2 * (int64_t)kPlanLdsSortMax;
+    int32_t* goff_ws = ws + a.tmp_off;  // [B+1] global tile offset of each request
+    int32_t* goff = in_lds ? lds_i : goff_ws;
+    int32_t* req_rd = in_lds ? lds_i + (B + 1) : req;
     for (int base = 0; base < B; base += blockDim.x) {
       const int b = base + threadIdx.x;
       const int64_t t = b < B ? (clamp_len(a.seq_lens[b], a.max_kv_len) + a.tile - 1) / a.tile : 0;
       int64_t tot;
       const int64_t ex = block_exclusive_scan(t, sh, &tot);
-      if (b < B) goff[b] = (int32_t)(carry + ex);
+      if (b < B) goff[b] = goff_ws[b] = (int32_t)(carry + ex);
       carry += tot;
     }
     const int64_t T = carry;
-    if (threadIdx.x == 0) goff[B] = (int32_t)T;
+    if (threadIdx.x == 0) goff[B] = goff_ws[B] = (int32_t)T;
     int64_t C = (T + a.target_items - 1) / a.target_items;
     C = C < 1 ? 1 : C;
     int64_t nchunks = (T + C - 1) / C;
@@ -139,25 +230,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
       int64_t tot;
       const int64_t ex = block_exclusive_scan(nseg, sh, &tot);
-      if (b < B) req[b] = (int32_t)(carry + ex);
+      if (b < B) req_rd[b] = req[b] = (int32_t)(carry + ex);
       carry += tot;
     }
-    if (threadIdx.x == 0) req[B] = (int32_t)carry;
+    if (threadIdx.x == 0) req_rd[B] = req[B] = (int32_t)carry;
     const int64_t num = carry < a.capacity ? carry : a.capacity;
     __threadfence_block();
     __syncthreads();
     // segments (b, kv_begin, kv_end, partial index) in request order, and
     // the chunk of each (non-decreasing along the list)
-    int32_t* seg_chunk = ws + a.keys_off;
+    int32_t* seg_chunk_ws = ws + a.keys_off;
+    int32_t* seg_chunk = in_lds ? lds_i + 2 * (B + 1) : seg_chunk_ws;
     for (int b = threadIdx.x; b < B; b += blockDim.x) {
       const int L = clamp_len(a.seq_lens[b], a.max_kv_len);
       const int64_t o = goff[b], t = goff[b + 1] - o;
-      const int first = req[b], n = req[b + 1] - req[b];
+      const int first = req_rd[b], n = req_rd[b + 1] - req_rd[b];
       if (t == 0) {
         if (first < num) {
           items[first] = make_int4(b, 0, 0, -1);
           const int64_t cc = o / C;
-          seg_chunk[first] = (int32_t)(cc < nchunks ? cc : nchunks - 1);
+          seg_chunk[first] = seg_chunk_ws[first] = (int32_t)(cc < nchunks ? cc : nchunks - 1);
         }
         continue;
       }
@@ -168,7 +260,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         const int kb = (int)((g0 - o) * a.tile);
         const int ke = (int)((g1 - o) * a.tile < L ? (g1 - o) * a.tile : L);
         items[first + sgi] = make_int4(b, kb, ke, n > 1 ? first + sgi : -1);
-        seg_chunk[first + sgi] = (int32_t)cc;
+        seg_chunk[first + sgi] = seg_chunk_ws[first + sgi] = (int32_t)cc;
       }
     }
     __threadfence_block();
@@ -326,7 +418,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(plan_decode_by_one_wave(a) ? 64 : kPlanThreads), 0, s, a);
   return hipGetLastError();
 }
 

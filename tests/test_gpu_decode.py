@@ -229,12 +229,16 @@ def test_plan_matches_oracle_rederivation_bit_for_bit():
     torch = torch_mod()
     pkv = _pkv()
     rng = np.random.default_rng(11)
-    for kv_chunk, target, fp8 in ((0, 0, False), (0, 100, False), (64, 0, False), (0, 50000, False),
-                                  (0, 0, True), (0, 300, True), (96, 0, True)):
-        B = 37
+    cases = ((0, 0, False), (0, 100, False), (64, 0, False), (0, 50000, False), (0, 0, True), (0, 300, True),
+             (96, 0, True))
+    # 37 and 64 requests take the one-wave plan, 150 the workgroup one; the
+    # 64-request batch has a run of empty requests
+    for B, (kv_chunk, target, fp8) in [(B, c) for B in (37, 150) for c in cases] + [(64, cases[0]), (64, cases[4])]:
         max_kv = 5000
         L = rng.integers(0, max_kv + 1, size=B).astype(np.int32)
         L[5] = max_kv + 100  # clamped
+        if B == 64:
+            L[20:29] = 0
         extra = dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=64, q_block=1) if fp8 else {}
         params = pkv.Params(32, 8, 128, 16, max_kv_len=max_kv, kv_chunk=kv_chunk, split_target=target, **extra)
         tile = 64 if fp8 else 32
