@@ -237,7 +237,8 @@ int pkv_kv_store(const pkv_params* params, void* k_pool, void* v_pool, int64_t p
                  const void* v_new, const int32_t* slots, int64_t num_tokens, void* stream) {
   // a plain row copy: the dtype rules of a decode plan cover both pool types
   if (int rc = check_params(params, PKV_DECODE)) return rc;
-  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens=%lld must be >= 0", (long long)num_tokens);
+  if (num_tokens < 0 || num_tokens > INT32_MAX)
+    return fail(PKV_EINVAL, "num_tokens=%lld must be in [0, 2^31)", (long long)num_tokens);
   if (pool_slots < 1) return fail(PKV_EINVAL, "pool_slots=%lld must be >= 1", (long long)pool_slots);
   if (num_tokens == 0) return ok();
   if (!k_pool || !v_pool || !k_new || !v_new || !slots) return fail(PKV_EINVAL, "a pool, new-row or slots pointer is NULL");

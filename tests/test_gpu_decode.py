@@ -263,13 +263,14 @@ def test_plan_matches_oracle_rederivation_bit_for_bit():
             assert np.array_equal(ws[ws[7]:ws[7] + ws[6] + 1], ref["chunk_tab"])
 
 
-def test_kv_store_round_trip_bit_exact():
+@pytest.mark.parametrize("hkv,d", [(4, 128), (40, 128), (2, 64), (1, 64)])
+def test_kv_store_round_trip_bit_exact(hkv, d):
     torch = torch_mod()
     pkv = _pkv()
-    spec = Spec("st", "extend", 6, 8, 4, 128, 16, (0, 100), (1, 40))
+    spec = Spec("st", "extend", 6, 2 * hkv, hkv, d, 16, (0, 100), (1, 40))
     hb = make_host_batch(spec, 9)
     lay = hb.layout
-    params = pkv.Params(8, 4, 128, 16, max_kv_len=lay.max_kv_len)
+    params = pkv.Params(2 * hkv, hkv, d, 16, max_kv_len=lay.max_kv_len)
     kp = dev_bf16(pool_before_store(hb.k_pool, lay.new_slots, fill=7.0))
     vp = dev_bf16(pool_before_store(hb.v_pool, lay.new_slots, fill=7.0))
     before_k = kp.clone()
@@ -282,6 +283,26 @@ def test_kv_store_round_trip_bit_exact():
     idx = dev_i32(untouched).long()
     # compare bit patterns: the untouched rows include NaN poison
     assert torch.equal(kp[idx].view(torch.int16), before_k[idx].view(torch.int16))
+
+
+def test_kv_store_skips_slots_outside_the_pool():
+    torch = torch_mod()
+    pkv = _pkv()
+    spec = Spec("st2", "extend", 4, 8, 4, 128, 16, (0, 50), (2, 20))
+    hb = make_host_batch(spec, 10)
+    lay = hb.layout
+    params = pkv.Params(8, 4, 128, 16, max_kv_len=lay.max_kv_len)
+    kp = dev_bf16(pool_before_store(hb.k_pool, lay.new_slots, fill=7.0))
+    vp = dev_bf16(pool_before_store(hb.v_pool, lay.new_slots, fill=7.0))
+    slots = lay.new_slots.copy()
+    bad = [0, 3, len(slots) - 1]
+    slots[bad[0]], slots[bad[1]], slots[bad[2]] = -1, lay.pool_slots, lay.pool_slots + 1000
+    pkv.kv_store(params, kp, vp, dev_bf16(hb.k_new), dev_bf16(hb.v_new), dev_i32(slots))
+    torch.cuda.synchronize()
+    k, v = host(kp), host(vp)
+    good = np.setdiff1d(np.arange(len(slots)), bad)
+    assert np.array_equal(k[slots[good]], hb.k_new[good]) and np.array_equal(v[slots[good]], hb.v_new[good])
+    assert np.all(k[lay.new_slots[bad]] == 7.0) and np.all(v[lay.new_slots[bad]] == 7.0)
 
 
 def _sampled_full_size(name, samples, kv_chunk=0):
