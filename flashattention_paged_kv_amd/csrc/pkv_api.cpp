@@ -49,6 +49,7 @@ int check_params(const pkv_params* p, int mode) {
   if (!is_pow2(p->page_size) || p->page_size > 256)
     return fail(PKV_EINVAL, "page_size=%d must be a power of two in [1, 256]", p->page_size);
   if (p->max_kv_len < 1) return fail(PKV_EINVAL, "max_kv_len=%d must be >= 1", p->max_kv_len);
+  if (p->max_kv_len > (1 << 30)) return fail(PKV_EUNSUPPORTED, "max_kv_len=%d exceeds 2^30", p->max_kv_len);
   if (p->kv_chunk < 0 || p->kv_chunk % pkv::kDecodeTile != 0)
     return fail(PKV_EINVAL, "kv_chunk=%d must be 0 or a positive multiple of %d", p->kv_chunk, pkv::kDecodeTile);
   if (p->split_target < 0) return fail(PKV_EINVAL, "split_target=%d must be >= 0", p->split_target);
@@ -161,6 +162,9 @@ int pkv_plan_metadata(const pkv_params* params, int32_t mode, int32_t batch, int
     return fail(PKV_EWORKSPACE, "workspace_bytes=%zu is smaller than the %lld bytes required", workspace_bytes,
                 (long long)(w.total_ints * 4));
   if (w.capacity > INT32_MAX) return fail(PKV_EUNSUPPORTED, "work-item capacity %lld exceeds int32", (long long)w.capacity);
+  if (mode == PKV_DECODE && (int64_t)batch * pkv::ceil_div(params->max_kv_len, pkv::decode_plan_tile(*params)) > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "batch=%d x max_kv_len=%d exceeds the plan's int32 tile offsets", batch,
+                params->max_kv_len);
   pkv::PlanArgs a{};
   a.seq_lens = seq_lens;
   a.cu_seqlens_q = cu_seqlens_q;

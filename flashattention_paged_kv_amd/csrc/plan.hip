@@ -91,11 +91,11 @@ __device__ void plan_decode_one_wave(const PlanArgs& a, int32_t* tab_lds) {
   const int B = a.batch, b = threadIdx.x;
   const bool on = b < B;
   const int L = on ? clamp_len(a.seq_lens[b], a.max_kv_len) : 0;
-  const int t = on ? (L + a.tile - 1) / a.tile : 0;
-  const int o = wave_inclusive_scan32(t) - t;
+  const int t = on ? L / a.tile + (L % a.tile != 0) : 0;
+  const int o = wave_inclusive_scan32(t) - t;  // the host keeps the batch's tiles below 2^31
   const int T = __shfl(o + t, 63, 64);
-  const int C = T > a.target_items ? (T + a.target_items - 1) / a.target_items : 1;
-  const int nchunks = T > C ? (T + C - 1) / C : 1;
+  const int C = T > a.target_items ? (int)(((int64_t)T + a.target_items - 1) / a.target_items) : 1;
+  const int nchunks = T > C ? (int)(((int64_t)T + C - 1) / C) : 1;
   const int nseg = on ? (t == 0 ? 1 : (o + t - 1) / C - o / C + 1) : 0;
   const int first = wave_inclusive_scan32(nseg) - nseg;
   const int total = __shfl(first + nseg, 63, 64);
@@ -118,10 +118,10 @@ __device__ void plan_decode_one_wave(const PlanArgs& a, int32_t* tab_lds) {
     } else {
       for (int sgi = 0; sgi < nseg && first + sgi < num; ++sgi) {
         const int cc = o / C + sgi;
-        const int g0 = o > cc * C ? o : cc * C;
-        const int g1 = o + t < (cc + 1) * C ? o + t : (cc + 1) * C;
-        const int kb = (g0 - o) * a.tile;
-        const int ke = (g1 - o) * a.tile < L ? (g1 - o) * a.tile : L;
+        const int64_t g0 = o > (int64_t)cc * C ? o : (int64_t)cc * C;
+        const int64_t g1 = (int64_t)o + t < ((int64_t)cc + 1) * C ? (int64_t)o + t : ((int64_t)cc + 1) * C;
+        const int kb = (int)((g0 - o) * a.tile);
+        const int ke = (int)((g1 - o) * a.tile < L ? (g1 - o) * a.tile : L);
         items[first + sgi] = make_int4(b, kb, ke, nseg > 1 ? first + sgi : -1);
         atomicMin(&tab_lds[cc], first + sgi);
       }
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int32_t* req_rd = in_lds ? lds_i + (B + 1) : req;
     for (int base = 0; base < B; base += blockDim.x) {
       const int b = base + threadIdx.x;
-      const int64_t t = b < B ? (clamp_len(a.seq_lens[b], a.max_kv_len) + a.tile - 1) / a.tile : 0;
+      const int64_t t = b < B ? ((int64_t)clamp_len(a.seq_lens[b], a.max_kv_len) + a.tile - 1) / a.tile : 0;
       int64_t tot;
       const int64_t ex = block_exclusive_scan(t, sh, &tot);
       if (b < B) goff[b] = goff_ws[b] = (int32_t)(carry + ex);
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       int b = base + threadIdx.x;
       int64_t splits = 0;
       if (b < B) {
-        int64_t tiles = (clamp_len(a.seq_lens[b], a.max_kv_len) + kDecodeTile - 1) / kDecodeTile;
+        int64_t tiles = ((int64_t)clamp_len(a.seq_lens[b], a.max_kv_len) + kDecodeTile - 1) / kDecodeTile;
         splits = (tiles + chunk - 1) / chunk;
         if (splits < 1) splits = 1;
       }

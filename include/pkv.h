@@ -95,7 +95,7 @@ typedef struct pkv_params {
   int32_t kv_dtype;     /* pkv_dtype; PKV_FP8_E4M3 needs head_dim 128 (and q_block 1 for EXTEND) */
   int32_t q_block;      /* 8-bit: q rows per sfQ block (DECODE: one row per request; EXTEND: 1); else 0 */
   int32_t k_block;      /* 8-bit: key positions per sfK block, a multiple of 16; else 0 */
-  int32_t max_kv_len;   /* upper bound of seq_lens (>= 1, <= rtt_stride of the run calls) */
+  int32_t max_kv_len;   /* upper bound of seq_lens (1 .. 2^30, <= rtt_stride of the run calls) */
   int32_t kv_chunk;     /* DECODE split size in tokens: 0 = automatic, else a multiple of 32 */
   int32_t split_target; /* DECODE automatic mode: waves per call to size splits for; 0 = as many
                            as the current device holds at once (from the kernel's occupancy;

@@ -143,6 +143,16 @@ def test_run_call_argument_errors(lib):
     assert rc == pkv.PKV_OK and pkv.last_error() == ""
 
 
+def test_length_bounds(lib):
+    rc, _, _ = _ws(lib, pkv.Params(32, 8, 128, 16, (1 << 30) + 1))
+    assert rc == pkv.PKV_EUNSUPPORTED and "2^30" in pkv.last_error()
+    # a decode batch whose total tiles would not fit the plan's int32 offsets
+    p = pkv.Params(32, 8, 128, 16, 1 << 30)
+    fake = ctypes.c_void_p(0x1000)
+    rc = lib.pkv_plan_metadata(ctypes.byref(p), pkv.PKV_DECODE, 64, 0, fake, None, fake, 1 << 40, None)
+    assert rc == pkv.PKV_EUNSUPPORTED and "int32 tile offsets" in pkv.last_error()
+
+
 def test_block_sparse_table_argument_errors(lib):
     p = pkv.Params(32, 8, 128, 16, 4096)
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
