@@ -385,7 +385,7 @@ RUNNERS = {"decode_bf16": DecodeRunner, "long_decode_bf16": DecodeRunner, "decod
            "decode_n4_bf16": DecodeRunner, "extend_bf16": ExtendRunner, "extend_fp8": ExtendRunner,
            "sparse_decode_bf16": SparseDecodeRunner, "sparse_decode_fp8": SparseDecodeRunner}
 UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "decode_fp8": "GB/s", "decode_n4_bf16": "GB/s",
-         "extend_bf16": "TFLOP/s", "extend_fp8": "TFLOP/s"}
+         "extend_bf16": "TFLOP/s", "extend_fp8": "TFLOP/s", "sparse_decode_bf16": "GB/s", "sparse_decode_fp8": "GB/s"}
 DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "decode_fp8": 4, "decode_n4_bf16": 4, "extend_bf16": 4,
                   "extend_fp8": 4, "sparse_decode_bf16": 2, "sparse_decode_fp8": 2}
 
