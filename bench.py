@@ -192,10 +192,14 @@ class DecodeRunner:
         for l in range(self.layers):
             pkv.kv_store(self.params, db.k_pools[l], db.v_pools[l], db.k_new[l], db.v_new[l], db.new_slots)
 
+    plan_per_layer = False  # --plan-per-layer: re-plan before every layer (the pattern the plan replaces)
+
     def attn(self):
         """Every layer's attention call, back to back."""
         pkv, db = self.pkv, self.db
         for l in range(self.layers):
+            if self.plan_per_layer:
+                self.plan = pkv.plan_metadata(self.params, pkv.PKV_DECODE, db.seq_lens, workspace=self.ws)
             pkv.attn_decode(self.params, db.q, db.k_pools[l], db.v_pools[l], db.req_to_token, db.seq_lens, self.plan,
                             scratch=self.scratch, out=self.out[l], lse=self.lse,
                             sfq=db.sfq, sfk=db.sfk, sfv=db.sfv)
@@ -347,6 +351,8 @@ class ExtendRunner:
         p = lay.prefix_lens.astype("int64")
         pairs = int((n * p + n * (n + 1) // 2).sum())  # unmasked (query, key) pairs per head
         self.flops_per_layer = 4 * spec.head_dim * spec.num_q_heads * pairs
+        # context only: the same rows against all of their request's keys, no causal mask
+        self.dense_equivalent_flops = 4 * spec.head_dim * spec.num_q_heads * int((n * (n + p)).sum())
         self.work_per_step = self.flops_per_layer * layers
 
     def pre(self):
@@ -370,7 +376,8 @@ class ExtendRunner:
         return {"workload": s.name, "batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
                 "head_dim": s.head_dim, "page_size": s.page_size, "prefix_len": f"U{list(s.prefix)}",
                 "new_len": f"U{list(s.new)}", "total_q": self.total_q, "layers_per_step": self.layers,
-                "kv_dtype": "fp8_e4m3" if self.fp8 else "bf16", "flops_per_layer": self.flops_per_layer}
+                "kv_dtype": "fp8_e4m3" if self.fp8 else "bf16", "flops_per_layer": self.flops_per_layer,
+                "dense_equivalent_flops_per_layer": self.dense_equivalent_flops}
 
     def roofline(self, avg_launch_s, workload):
         achieved = self.flops_per_layer / avg_launch_s / 1e12
@@ -459,6 +466,8 @@ def main():
                     help="replay the step as captured HIP graphs (plan + stores, then the attention calls) "
                          "instead of launching every kernel from Python")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the 1 GiB copy (counter calibration)")
+    ap.add_argument("--plan-per-layer", action="store_true",
+                    help="decode: plan before every layer instead of once per batch (for comparison only)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV files (host only)")
     ap.add_argument("--commands", default="", help="with --ingest-counters: the profiler commands, ' ;; '-separated")
@@ -481,13 +490,15 @@ def main():
 
     pkv.load_library()  # fails loudly when the HIP library is missing
     graph = args.graph
+    DecodeRunner.plan_per_layer = args.plan_per_layer
     runner, ms, value, roof = measure(args.workload, args.steps, args.warmup, args.layers, torch, pkv, workloads,
                                       graph=graph)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": UNITS[args.workload], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3" if getattr(runner, "fp8", False) else "bf16",
-        "data": "synthetic", "config": runner.describe(), "launch": "hip_graph" if graph else "eager",
+        "data": "synthetic", "config": runner.describe(),
+        "launch": ("hip_graph" if graph else "eager") + (", plan per layer" if args.plan_per_layer else ""),
         "roofline": roof,
     }
     secondary = {}
