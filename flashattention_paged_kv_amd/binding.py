@@ -210,8 +210,8 @@ def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan:
         nblk = -(-params.max_kv_len // params.k_block)
         if tuple(sfk.shape) != (B, params.num_kv_heads, nblk):
             raise ValueError(f"sfk must be [B, Hkv, ceil(max_kv_len/k_block)] = {(B, params.num_kv_heads, nblk)}")
-        if sfq is None or tuple(sfq.shape) != (B, params.num_q_heads):
-            raise ValueError("sfq must be [B, Hq]")
+        if sfq is None or tuple(sfq.shape) != (B * n, params.num_q_heads):
+            raise ValueError("sfq must be [B * decode_q_len, Hq] (one scale per new-token row and head)")
         if sfv is None or tuple(sfv.shape) != (B, params.num_kv_heads, params.head_dim):
             raise ValueError("sfv must be [B, Hkv, d]")
         if v_mean is not None and tuple(v_mean.shape) != (B, params.num_kv_heads, params.head_dim):

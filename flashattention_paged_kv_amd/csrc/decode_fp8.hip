@@ -11,8 +11,10 @@
 // the accumulator is rescaled in fp32 when the max grows.
 //
 // Same decomposition as the bf16 decode (one wave per (request, split, kv
-// head, 16-head group); a request with several splits is merged by
-// decode_merge_kernel), with 64-token tiles and the gfx950 fp8 MFMA
+// head, group of 16 (new token, head) columns); a request with several
+// splits is merged by decode_merge_kernel; with several new tokens per
+// request each column has its own causal limit and sfQ row), with 64-token
+// tiles and the gfx950 fp8 MFMA
 // 16x16x128 (f8f6f4, unit block scales):
 //  * Sᵀ = K8·Q8ᵀ: one MFMA per 16 keys covers all 128 channels (each lane
 //    holds 32 bytes of one key row);
@@ -92,25 +94,27 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 
 }  // namespace
 
-// Q8 of request b as the B operand (lane holds q8[h][32 j .. 32 j + 32]) and
-// the score factor sm_scale·log2(e)·sfQ[b,h].
-__device__ __forceinline__ void load_q8(const DecodeArgs& a, i32x8& qop, float& qscale, int b, int h, bool head_ok,
-                                        int j) {
+// Q8 of new token qi of request b as the B operand (lane holds
+// q8[row][h][32 j .. 32 j + 32], row = b·q_len + qi) and the score factor
+// sm_scale·log2(e)·sfQ[row, h].
+__device__ __forceinline__ void load_q8(const DecodeArgs& a, i32x8& qop, float& qscale, int b, int qi, int h,
+                                        bool head_ok, int j) {
   constexpr int D = 128;
   h = opaque(h);
   j = opaque(j);
-  const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + ((int64_t)b * a.hq + h) * D + 32 * j;
+  const int64_t row = ((int64_t)b * a.q_len + (head_ok ? qi : 0)) * a.hq + h;
+  const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + row * D + 32 * j;
   const u32x4 z = {0u, 0u, 0u, 0u};
   const u32x4 q0 = head_ok ? ldg16(qrow) : z, q1 = head_ok ? ldg16(qrow + 16) : z;
   qop = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3], (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
-  qscale = head_ok ? a.sfq[(int64_t)b * a.hq + h] * a.scale_log2 : 0.f;
+  qscale = head_ok ? a.sfq[row] * a.scale_log2 : 0.f;
 }
 
 // Applies the per-channel V scale (and mean) to one segment's accumulator and
 // writes it: bf16 O and lse for a request covered by one segment, else the
 // fp32 partial and its log2-sum-exp.
 __device__ __forceinline__ void finish_segment8(const DecodeArgs& a, int b, int g, int part, float m, float lpart,
-                                                const floatx4 (&acc)[8], int h, bool head_ok, int j) {
+                                                const floatx4 (&acc)[8], int qi, int h, bool head_ok, int j) {
   constexpr int D = 128;
   h = opaque(h);
   j = opaque(j);
@@ -131,7 +135,7 @@ __device__ __forceinline__ void finish_segment8(const DecodeArgs& a, int b, int 
     }
   if (part < 0) {
     if (head_ok) {
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.hq + h) * D;
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + (((int64_t)b * a.q_len + qi) * a.hq + h) * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         u32x4 w;
@@ -139,31 +143,31 @@ __device__ __forceinline__ void finish_segment8(const DecodeArgs& a, int b, int 
         for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(o[r][2 * k], o[r][2 * k + 1]);
         stg16(orow + 32 * j + 8 * r, w);
       }
-      if (j == 0 && a.lse) a.lse[(int64_t)b * a.hq + h] = lse2 * kLn2;
+      if (j == 0 && a.lse) a.lse[((int64_t)b * a.q_len + qi) * a.hq + h] = lse2 * kLn2;
     }
     return;
   }
   if (head_ok) {
-    float* po = a.part_o + ((int64_t)part * a.hq + h) * D;
+    float* po = a.part_o + (((int64_t)part * a.q_len + qi) * a.hq + h) * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r) = floatx4{o[r][0], o[r][1], o[r][2], o[r][3]};
       *reinterpret_cast<floatx4*>(po + 32 * j + 8 * r + 4) = floatx4{o[r][4], o[r][5], o[r][6], o[r][7]};
     }
-    if (j == 0) a.part_lse[(int64_t)part * a.hq + h] = lse2;
+    if (j == 0) a.part_lse[((int64_t)part * a.q_len + qi) * a.hq + h] = lse2;
   }
 }
 
 // Empty segments (requests with no KV) in [from, to): the epilogue of an
 // empty sum, so O = v_mean (0 without it) and lse = -inf.
 __device__ __forceinline__ void finish_empty8(const DecodeArgs& a, SegWindow& w, int from, int to, int s1, int g,
-                                              int h, bool head_ok, int j, int lane) {
+                                              int qi, int h, bool head_ok, int j, int lane) {
   floatx4 zero[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) zero[c] = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int s = from; s < to; ++s) {
     const TileCursor e = seg_at(a, w, s, s1, lane);
-    finish_segment8(a, e.b, g, e.part, kNegInf, 0.f, zero, h, head_ok, j);
+    finish_segment8(a, e.b, g, e.part, kNegInf, 0.f, zero, qi, h, head_ok, j);
   }
 }
 
@@ -178,8 +182,11 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
   const int g = unit / a.head_groups, hg = unit - g * a.head_groups;
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, j = lane >> 4;
-  const int hl = hg * 16 + l16;
-  const bool head_ok = hl < a.group;
+  // MFMA column = (new token qi, head hl of the group), token-major
+  const int col = hg * 16 + l16;
+  const int qi = col / a.group;
+  const int hl = col - qi * a.group;
+  const bool head_ok = qi < a.q_len;
   const int h = g * a.group + (head_ok ? hl : 0);
   const uint32_t row_bytes = (uint32_t)a.hkv * D;
   const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k_pool) + (int64_t)g * D;
@@ -194,12 +201,12 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
   TileCursor C = seg_at(a, w, s0, s1, lane);
   C.t0 -= kTile8;
   C = next_tile<kTile8>(a, w, C, s1, lane);
-  finish_empty8(a, w, s0, C.seg, s1, g, h, head_ok, j, lane);
+  finish_empty8(a, w, s0, C.seg, s1, g, qi, h, head_ok, j, lane);
   if (C.seg >= s1) return;
 
   i32x8 qop;
   float qscale;
-  load_q8(a, qop, qscale, C.b, h, head_ok, j);
+  load_q8(a, qop, qscale, C.b, qi, h, head_ok, j);
   float m = kNegInf, lpart = 0.f;
   floatx4 acc[8];
 #pragma unroll
@@ -223,14 +230,17 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
     mx = max_xor32(max_xor16(mx));
-    const float m_new = fmaxf(m, mx);  // finite: key t0 is in range
-    const float alpha = exp2_fast(m - m_new);
+    // -inf only for a column that has seen no key yet (a new token whose
+    // causal limit lies below this tile); it then keeps zero weight
+    const float m_new = fmaxf(m, mx);
+    const float alpha = m_new == kNegInf ? 1.f : exp2_fast(m - m_new);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
     m = m_new;
     float p[16];
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      p[e] = exp2_fast(sc[e] - m_new);
+      p[e] = exp2_fast(sc[e] - m_use);
       ps += p[e];
     }
     lpart = lpart * alpha + ps;
@@ -279,10 +289,10 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
     L = S;
     S = next_tile<kTile8>(a, w, S, s1, lane);
     if (C.seg == prev.seg) return true;
-    finish_segment8(a, prev.b, g, prev.part, m, lpart, acc, h, head_ok, j);
-    finish_empty8(a, w, prev.seg + 1, C.seg, s1, g, h, head_ok, j, lane);
+    finish_segment8(a, prev.b, g, prev.part, m, lpart, acc, qi, h, head_ok, j);
+    finish_empty8(a, w, prev.seg + 1, C.seg, s1, g, qi, h, head_ok, j, lane);
     if (C.seg >= s1) return false;
-    load_q8(a, qop, qscale, C.b, h, head_ok, j);
+    load_q8(a, qop, qscale, C.b, qi, h, head_ok, j);
     m = kNegInf;
     lpart = 0.f;
 #pragma unroll
@@ -294,12 +304,12 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
     s_even = slot_at(rtt_of(S), S.t0, S.kv_end, last, lane);
     load_tile8(tb, s_odd, L.t0, L.kv_end, sfk_of(L), a.k_block, kbase, vbase, row_bytes, lane);
     __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
-    compute(ta, C.t0, C.kv_end);
+    compute(ta, C.t0, min(C.kv_end, C.lim + qi + 1));
     if (!advance()) break;
     s_odd = slot_at(rtt_of(S), S.t0, S.kv_end, last, lane);
     load_tile8(ta, s_even, L.t0, L.kv_end, sfk_of(L), a.k_block, kbase, vbase, row_bytes, lane);
     __builtin_amdgcn_sched_barrier(0);
-    compute(tb, C.t0, C.kv_end);
+    compute(tb, C.t0, min(C.kv_end, C.lim + qi + 1));
     if (!advance()) break;
   }
 }

@@ -57,8 +57,6 @@ int check_params(const pkv_params* p, int mode) {
     return fail(PKV_EINVAL, "decode_q_len=%d must be in [0, 64]", p->decode_q_len);
   if (p->decode_q_len > 1 && mode != PKV_DECODE)
     return fail(PKV_EINVAL, "decode_q_len applies to DECODE plans only (EXTEND takes cu_seqlens_q)");
-  if (p->decode_q_len > 1 && p->kv_dtype != PKV_BF16)
-    return fail(PKV_EUNSUPPORTED, "decode_q_len > 1 is unsupported with kv_dtype=%d", p->kv_dtype);
   if (p->kv_dtype == PKV_BF16) {
     // block sizes only exist for the 8-bit recipe: reject them like an
     // inapplicable plan input (FlashInfer Sage page, code §2)

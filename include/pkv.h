@@ -103,7 +103,8 @@ typedef struct pkv_params {
   int32_t decode_q_len; /* DECODE: new tokens per request, n in [1, 64] (0 means 1).  With n > 1
                            (e.g. verifying n drafted tokens) q and out are [B*n, Hq, d], rows
                            request-major, and new token i of request b attends to keys
-                           0 .. L_b - n + i (bottom-right causal, as EXTEND); bf16 only */
+                           0 .. L_b - n + i (bottom-right causal, as EXTEND); on the 8-bit path
+                           sfq holds one scale per new-token row, [B*n, Hq] */
 } pkv_params;
 
 /* Sizes of the plan workspace (written by pkv_plan_metadata, read by the run
@@ -165,12 +166,13 @@ int pkv_block_sparse_table(const pkv_params* params, int32_t batch, const int32_
                            int32_t block_size, const float* sfk, int32_t* sparse_req_to_token,
                            int32_t* sparse_seq_lens, float* sparse_sfk, void* stream);
 
-/* DECODE: one query row per request (q, out: [B, Hq, d]).  bf16 path: q and
+/* DECODE: one query row per request (q, out: [B, Hq, d]; [B*n, Hq, d] with
+ * params->decode_q_len = n).  bf16 path: q and
  * pools bf16, sfq/sfk/sfv/v_mean must be NULL.  8-bit path (kv_dtype ==
  * PKV_FP8_E4M3): q and pools hold E4M3 bytes and the Sage formula applies:
  * S = sm_scale·sfq[b,h]·sfk[b,g,j/k_block]·(q8·k8), P stored as E4M3 of
  * 448·exp(S - m), O = sfv[b,g,:]·(Σ P8·v8)/(448·l) (+ v_mean[b,g,:]), where l
- * sums the unquantised exp(S - m).  sfq float [B, Hq], sfk float
+ * sums the unquantised exp(S - m).  sfq float [B*decode_q_len, Hq], sfk float
  * [B, Hkv, sfk_stride] with sfk_stride = ceil(max_kv_len / k_block), sfv and
  * v_mean float [B, Hkv, d]; v_mean may be NULL.  Scale values are not checked.
  * `workspace` comes from pkv_plan_metadata(PKV_DECODE) for this batch;

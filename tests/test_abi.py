@@ -52,7 +52,6 @@ def _ws(lib, params, mode=pkv.PKV_DECODE, batch=4, total_q=0):
     (dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=64, q_block=1, head_dim=64), pkv.PKV_EUNSUPPORTED, "head_dim=128"),
     (dict(decode_q_len=-1), pkv.PKV_EINVAL, "decode_q_len=-1"),
     (dict(decode_q_len=65), pkv.PKV_EINVAL, "decode_q_len=65"),
-    (dict(decode_q_len=4, kv_dtype=pkv.PKV_FP8_E4M3, k_block=64, q_block=1), pkv.PKV_EUNSUPPORTED, "decode_q_len > 1"),
 ])
 def test_params_validation(lib, kw, code, msg):
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_kv_len=4096)

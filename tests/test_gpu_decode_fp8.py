@@ -133,3 +133,48 @@ def test_full_size_fp8_decode_sampled():
         got.append(host(out[b:b + 1]))
         ref.append(o)
         assert rel_l2(got[-1], o) <= FP8_REL_L2, b
+
+
+def run_fp8_multi(hb, n, v_mean=None, kv_chunk=0, seed=None):
+    """n new tokens per request in one 8-bit decode call, with one sfQ per
+    new-token row (the request's scale times a per-row factor, so the row
+    indexing is exercised).  Returns host (o, lse, the per-row sfQ)."""
+    torch = torch_mod()
+    pkv = _pkv()
+    lay = hb.layout
+    spec = lay.spec
+    B, hq, hkv = spec.batch, spec.num_q_heads, spec.num_kv_heads
+    rng = np.random.default_rng(n if seed is None else seed)
+    sfq_rows = (hb.sfq[np.repeat(np.arange(B), n)] * rng.uniform(0.8, 1.25, (B * n, hq))).astype(np.float32)
+    k_pool = dev_u8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F))
+    v_pool = dev_u8(pool_before_store(hb.v_codes, lay.new_slots, fill=0x7F))
+    params = pkv.Params(hq, hkv, 128, spec.page_size, max_kv_len=lay.req_to_token.shape[1],
+                        kv_dtype=pkv.PKV_FP8_E4M3, q_block=1, k_block=spec.k_block, kv_chunk=kv_chunk,
+                        decode_q_len=n)
+    seq = dev_i32(lay.seq_lens)
+    plan = pkv.plan_metadata(params, pkv.PKV_DECODE, seq)
+    pkv.kv_store(params, k_pool, v_pool, dev_u8(hb.k_new_codes), dev_u8(hb.v_new_codes), dev_i32(lay.new_slots))
+    lse = torch.empty((B * n, hq), dtype=torch.float32, device="cuda")
+    out = pkv.attn_decode(params, dev_u8(hb.q_codes), k_pool, v_pool, dev_i32(lay.req_to_token), seq, plan, lse=lse,
+                          sfq=dev_f32(sfq_rows), sfk=dev_f32(hb.sfk), sfv=dev_f32(hb.sfv),
+                          v_mean=None if v_mean is None else dev_f32(v_mean))
+    torch.cuda.synchronize()
+    return host(out), lse.cpu().numpy().astype(np.float64), sfq_rows
+
+
+@pytest.mark.parametrize("n,hq,hkv,kv_chunk,with_vm", [(2, 32, 8, 0, False), (4, 32, 8, 0, True), (8, 8, 8, 0, False),
+                                                     (3, 16, 2, 128, True), (16, 8, 1, 0, False), (5, 40, 8, 64, False)])
+def test_fp8_several_new_tokens_per_request(n, hq, hkv, kv_chunk, with_vm):
+    """n new tokens per request checked in one 8-bit decode call: new token i
+    sees keys 0 .. L - n + i, one sfQ per new-token row; the oracle is the
+    8-bit extend formula with n rows per request."""
+    spec = Spec("f8_multi", "decode", 5, hq, hkv, 128, 16, (0, 900), n, dtype="fp8", k_block=64)
+    hb = make_host_batch(spec, 20 + n)
+    lay = hb.layout
+    vm = np.random.default_rng(100 + n).standard_normal((spec.batch, hkv, 128)).astype(np.float32) if with_vm else None
+    o, l, sfq_rows = run_fp8_multi(hb, n, v_mean=vm, kv_chunk=kv_chunk)
+    ro, rl = oracle.sage_extend(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens,
+                                lay.cu_seqlens_q, sfq_rows, hb.sfk, hb.sfv, spec.k_block, v_mean=vm)
+    assert np.all(np.isfinite(o))
+    assert rel_l2(o, ro) <= FP8_REL_L2, rel_l2(o, ro)
+    assert np.abs(l - rl).max() <= 1e-3

@@ -5,6 +5,7 @@ cases with combinations nobody chose; a failure prints the case."""
 import numpy as np
 import pytest
 
+import oracle
 from gpu_util import FP8_REL_L2, assert_bf16_close, assert_lse_close, rel_l2
 from workloads import Spec, make_host_batch
 
@@ -78,7 +79,19 @@ def test_random_fp8_decode_and_extend():
         hb = make_host_batch(spec, case)
         vm = rng.standard_normal((B, hkv, d)).astype(np.float32) if case % 3 == 0 else None
         what = f"case {case}: {mode} B={B} hq={hq} hkv={hkv} page={page} k_block={k_block} v_mean={vm is not None}"
-        if mode == "decode":
+        if mode == "decode" and case % 4 == 2:
+            # several new tokens per request: the extend formula with n rows each
+            from test_gpu_decode_fp8 import run_fp8_multi
+            n = int(rng.choice([2, 3, 4]))
+            spec = Spec(f"r8m{case}", "decode", B, hq, hkv, d, page, _lengths(rng, B, 0, 600), n, dtype="fp8",
+                        k_block=k_block)
+            hb = make_host_batch(spec, case)
+            what += f" n={n}"
+            o, lse, sfq_rows = run_fp8_multi(hb, n, v_mean=vm)
+            lay = hb.layout
+            ro, rlse = oracle.sage_extend(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens,
+                                          lay.cu_seqlens_q, sfq_rows, hb.sfk, hb.sfv, k_block, v_mean=vm)
+        elif mode == "decode":
             o, lse = run_fp8(hb, v_mean=vm)
             ro, rlse = oracle_fp8(hb, v_mean=vm)
         else:
