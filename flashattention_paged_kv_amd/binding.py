@@ -69,8 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]
     lib.pkv_attn_extend.argtypes = [pp, _P, _P, _P, _P, _P, _I64, _P, _I64, _P, _P, _P, _I32, _I64,
                                     _F, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]
-    for f in ("pkv_workspace_size", "pkv_plan_metadata", "pkv_kv_store", "pkv_attn_decode",
-              "pkv_attn_extend", "pkv_version"):
+    for f in ("pkv_workspace_size", "pkv_plan_metadata", "pkv_kv_store", "pkv_block_sparse_table",
+              "pkv_attn_decode", "pkv_attn_extend", "pkv_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []
@@ -107,6 +107,15 @@ def _need(t, name, dtype=None, ndim=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _need_rows(t, name, params: Params):
+    """K/V pools and new rows: [n, Hkv, d] of the params' element type."""
+    _need(t, name, ndim=3)
+    esize = 1 if params.kv_dtype == PKV_FP8_E4M3 else 2
+    if tuple(t.shape[1:]) != (params.num_kv_heads, params.head_dim) or t.element_size() != esize:
+        raise ValueError(f"{name} must be [n, {params.num_kv_heads}, {params.head_dim}] with {esize}-byte elements, "
+                         f"got {tuple(t.shape)} with {t.element_size()}-byte elements")
 
 
 def workspace_size(params: Params, mode: int, max_batch: int, max_total_q: int = 0) -> Tuple[int, int]:
@@ -146,7 +155,7 @@ def plan_metadata(params: Params, mode: int, seq_lens, cu_seqlens_q=None, total_
 def kv_store(params: Params, k_pool, v_pool, k_new, v_new, slots):
     import torch
     for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (k_new, "k_new"), (v_new, "v_new")):
-        _need(t, n, ndim=3)
+        _need_rows(t, n, params)
     _need(slots, "slots", torch.int32, 1)
     if k_new.shape[0] != slots.shape[0] or v_new.shape[0] != slots.shape[0]:
         raise ValueError("k_new/v_new rows must match slots")
@@ -194,7 +203,9 @@ def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan:
                 sfq=None, sfk=None, sfv=None, v_mean=None):
     """Decode attention: q [B, Hq, d] (bf16, or uint8 E4M3 codes) -> out [B, Hq, d] bf16."""
     import torch
-    _need(q, "q", ndim=3)
+    _need(q, "q", torch.uint8 if params.kv_dtype == PKV_FP8_E4M3 else torch.bfloat16, 3)
+    _need_rows(k_pool, "k_pool", params)
+    _need_rows(v_pool, "v_pool", params)
     _need(req_to_token, "req_to_token", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     _need(req_pool_indices, "req_pool_indices", torch.int32, 1)
@@ -241,6 +252,8 @@ def attn_extend(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, cu_se
     import torch
     fp8 = params.kv_dtype == PKV_FP8_E4M3
     _need(q, "q", torch.uint8 if fp8 else torch.bfloat16, 3)
+    _need_rows(k_pool, "k_pool", params)
+    _need_rows(v_pool, "v_pool", params)
     for t, nm in ((sfq, "sfq"), (sfk, "sfk"), (sfv, "sfv"), (v_mean, "v_mean")):
         _need(t, nm, torch.float32)
     _need(req_to_token, "req_to_token", torch.int32, 2)
