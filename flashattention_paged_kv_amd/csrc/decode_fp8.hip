@@ -176,6 +176,9 @@ __device__ __forceinline__ void finish_empty8(const DecodeArgs& a, SegWindow& w,
 // decode: while tile i is computed the rows of tile i+1 are in flight and
 // the slots of tile i+2 were requested before them, whichever segments the
 // tiles belong to.
+// MULTI: several new tokens per request (per-lane causal limits); the
+// one-token instance keeps none of that state in the tile loop.
+template <bool MULTI>
 __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, int s1, int unit, int4* win_rec,
                                                  int2* win_req) {
   constexpr int D = 128;
@@ -184,9 +187,9 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
   const int l16 = lane & 15, j = lane >> 4;
   // MFMA column = (new token qi, head hl of the group), token-major
   const int col = hg * 16 + l16;
-  const int qi = col / a.group;
-  const int hl = col - qi * a.group;
-  const bool head_ok = qi < a.q_len;
+  const int qi = MULTI ? col / a.group : 0;
+  const int hl = MULTI ? col - qi * a.group : col;
+  const bool head_ok = MULTI ? qi < a.q_len : hl < a.group;
   const int h = g * a.group + (head_ok ? hl : 0);
   const uint32_t row_bytes = (uint32_t)a.hkv * D;
   const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k_pool) + (int64_t)g * D;
@@ -232,9 +235,9 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
     mx = max_xor32(max_xor16(mx));
     // -inf only for a column that has seen no key yet (a new token whose
     // causal limit lies below this tile); it then keeps zero weight
-    const float m_new = fmaxf(m, mx);
-    const float alpha = m_new == kNegInf ? 1.f : exp2_fast(m - m_new);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float m_new = fmaxf(m, mx);  // one token per request: finite, key t0 is in range
+    const float alpha = (MULTI && m_new == kNegInf) ? 1.f : exp2_fast(m - m_new);
+    const float m_use = (MULTI && m_new == kNegInf) ? 0.f : m_new;
     m = m_new;
     float p[16];
     float ps = 0.f;
@@ -304,18 +307,18 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
     s_even = slot_at(rtt_of(S), S.t0, S.kv_end, last, lane);
     load_tile8(tb, s_odd, L.t0, L.kv_end, sfk_of(L), a.k_block, kbase, vbase, row_bytes, lane);
     __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
-    compute(ta, C.t0, min(C.kv_end, C.lim + qi + 1));
+    compute(ta, C.t0, MULTI ? min(C.kv_end, C.lim + qi + 1) : C.kv_end);
     if (!advance()) break;
     s_odd = slot_at(rtt_of(S), S.t0, S.kv_end, last, lane);
     load_tile8(ta, s_even, L.t0, L.kv_end, sfk_of(L), a.k_block, kbase, vbase, row_bytes, lane);
     __builtin_amdgcn_sched_barrier(0);
-    compute(tb, C.t0, min(C.kv_end, C.lim + qi + 1));
+    compute(tb, C.t0, MULTI ? min(C.kv_end, C.lim + qi + 1) : C.kv_end);
     if (!advance()) break;
   }
 }
 
 // WPB units of one chunk per workgroup, as in the bf16 decode.
-template <int WPB>
+template <int WPB, bool MULTI>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_fp8_kernel(DecodeArgs a) {
   const int32_t* __restrict__ ws = a.ws;
   // 1-D grid, unit group fastest: the workgroups of one chunk are
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
   const int s0 = tab ? ws[tab + c] : c, s1 = tab ? ws[tab + c + 1] : c + 1;
   __shared__ int4 win_rec[WPB][64];
   __shared__ int2 win_req[WPB][64];
-  decode_fp8_chunk(a, s0, s1, unit, win_rec[wv], win_req[wv]);
+  decode_fp8_chunk<MULTI>(a, s0, s1, unit, win_rec[wv], win_req[wv]);
 }
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch, hipStream_t s) {
@@ -340,15 +343,20 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity
   const int wpb = decode_waves_per_block(units);
   dim3 grid((unsigned)(capacity * ceil_div(units, wpb)));
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * wpb), 0, s, a); };
-  if (wpb == 8) go(decode_fp8_kernel<8>); else if (wpb == 4) go(decode_fp8_kernel<4>);
-  else if (wpb == 2) go(decode_fp8_kernel<2>); else go(decode_fp8_kernel<1>);
+  if (a.q_len > 1) {
+    if (wpb == 8) go(decode_fp8_kernel<8, true>); else if (wpb == 4) go(decode_fp8_kernel<4, true>);
+    else if (wpb == 2) go(decode_fp8_kernel<2, true>); else go(decode_fp8_kernel<1, true>);
+  } else {
+    if (wpb == 8) go(decode_fp8_kernel<8, false>); else if (wpb == 4) go(decode_fp8_kernel<4, false>);
+    else if (wpb == 2) go(decode_fp8_kernel<2, false>); else go(decode_fp8_kernel<1, false>);
+  }
   return hipGetLastError();
 }
 
 hipError_t decode_fp8_resident_items(int units, int64_t* items) {
   const int wpb = decode_waves_per_block(units);
-  const void* k = wpb == 8 ? (const void*)decode_fp8_kernel<8> : wpb == 4 ? (const void*)decode_fp8_kernel<4>
-                : wpb == 2 ? (const void*)decode_fp8_kernel<2> : (const void*)decode_fp8_kernel<1>;
+  const void* k = wpb == 8 ? (const void*)decode_fp8_kernel<8, false> : wpb == 4 ? (const void*)decode_fp8_kernel<4, false>
+                : wpb == 2 ? (const void*)decode_fp8_kernel<2, false> : (const void*)decode_fp8_kernel<1, false>;
   return resident_items_of(k, wpb, units, items);
 }
 
