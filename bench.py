@@ -83,14 +83,14 @@ def traffic_from_counters(workload: str):
 
 # Kernels that make up one attention call of each workload, as rocprofv3 names them.
 CALL_KERNELS = {
-    "decode_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
-    "long_decode_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
-    "decode_fp8": ("decode_fp8_kernel", "decode_merge_kernel"),
-    "decode_n4_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
+    "decode_bf16": ("decode_bf16_kernel", "decode_merge"),
+    "long_decode_bf16": ("decode_bf16_kernel", "decode_merge"),
+    "decode_fp8": ("decode_fp8_kernel", "decode_merge"),
+    "decode_n4_bf16": ("decode_bf16_kernel", "decode_merge"),
     "extend_bf16": ("extend_bf16_kernel",),
     "extend_fp8": ("extend_fp8_kernel",),
-    "sparse_decode_bf16": ("decode_bf16_kernel", "decode_merge_kernel"),
-    "sparse_decode_fp8": ("decode_fp8_kernel", "decode_merge_kernel"),
+    "sparse_decode_bf16": ("decode_bf16_kernel", "decode_merge"),
+    "sparse_decode_fp8": ("decode_fp8_kernel", "decode_merge"),
 }
 COPY_BYTES = 1 << 30
 

@@ -281,11 +281,21 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
   decode_chunk<D>(a, s0, s1, unit, win_rec[wv], win_req[wv]);
 }
 
-hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int32_t batch, hipStream_t s) {
+hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
+                               hipStream_t s) {
   if (batch <= 0) return hipSuccess;
   dim3 grid((unsigned)batch, (unsigned)(a.q_len * a.hq));
-  if (head_dim == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(kMergeThreads), 0, s, a);
-  else hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(kMergeThreads), 0, s, a);
+  const int nw = merge_waves(capacity, batch);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * nw), 0, s, a); };
+  if (head_dim == 128) {
+    if (nw == 8) go(decode_merge_many_kernel<128, 8>);
+    else if (nw == 4) go(decode_merge_many_kernel<128, 4>);
+    else go(decode_merge_few_kernel<128>);
+  } else {
+    if (nw == 8) go(decode_merge_many_kernel<64, 8>);
+    else if (nw == 4) go(decode_merge_many_kernel<64, 4>);
+    else go(decode_merge_few_kernel<64>);
+  }
   return hipGetLastError();
 }
 

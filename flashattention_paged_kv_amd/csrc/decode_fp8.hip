@@ -12,7 +12,7 @@
 //
 // Same decomposition as the bf16 decode (one wave per (request, split, kv
 // head, group of 16 (new token, head) columns); a request with several
-// splits is merged by decode_merge_kernel; with several new tokens per
+// splits is merged by the kernels of decode_merge.h; with several new tokens per
 // request each column has its own causal limit and sfQ row), with 64-token
 // tiles and the gfx950 fp8 MFMA
 // 16x16x128 (f8f6f4, unit block scales):

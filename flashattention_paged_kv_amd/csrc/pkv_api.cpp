@@ -327,7 +327,7 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
   hipError_t e = fp8 ? pkv::launch_decode_fp8(a, params->head_dim, w.capacity, batch, s)
                      : pkv::launch_decode_bf16(a, params->head_dim, w.capacity, batch, s);
   if (e != hipSuccess) return check_launch(e, "attn_decode launch");
-  return check_launch(pkv::launch_decode_merge(a, params->head_dim, batch, s), "attn_decode merge launch");
+  return check_launch(pkv::launch_decode_merge(a, params->head_dim, w.capacity, batch, s), "attn_decode merge launch");
 }
 
 int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void* q, const void* k_pool,

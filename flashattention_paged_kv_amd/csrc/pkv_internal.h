@@ -223,7 +223,8 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacit
                               hipStream_t s);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
                              hipStream_t s);
-hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int32_t batch, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
+                               hipStream_t s);
 // Work items (all their waves) of a decode launch that the current device
 // holds at once, from the kernel's occupancy and the CU count.
 hipError_t decode_bf16_resident_items(int head_dim, int units, int64_t* items);

@@ -71,18 +71,29 @@ __device__ __forceinline__ int wave_inclusive_scan32(int v) {
   return v;
 }
 
+// LDS words the one-wave decode plan keeps per batch ahead of its chunk table.
+constexpr int kOneWaveReqWords = 4 * 65;
+
 // Whether the one-wave decode plan below applies (decided on the host too).
 __host__ __device__ __forceinline__ bool plan_decode_by_one_wave(const PlanArgs& a) {
-  return a.mode == PKV_DECODE && a.kv_chunk == 0 && a.batch <= 64 && a.capacity < 2 * (int64_t)kPlanLdsSortMax;
+  return a.mode == PKV_DECODE && a.kv_chunk == 0 && a.batch <= 64 &&
+         a.capacity + 1 + kOneWaveReqWords <= 2 * (int64_t)kPlanLdsSortMax;
 }
 
 // Balanced decode chunks for at most 64 requests, by one wave (one lane per
-// request, 32-bit scans, no workgroup barrier): the same work list, offsets
-// and chunk table as the workgroup path below.  The chunk table is built in
-// LDS (`tab_lds`, nchunks + 1 <= capacity + 1 entries): every segment lowers
-// its chunk's entry to its own index, so an entry ends as the chunk's first
+// request for the scans, then the segments spread over all lanes; 32-bit
+// arithmetic, no workgroup barrier): the same work list, offsets and chunk
+// table as the workgroup path below.  LDS holds the requests' segment
+// offsets, tile offsets, tile counts and lengths (4 x 65 words) and then the
+// chunk table (nchunks + 1 <= capacity + 1 entries): every segment lowers its
+// chunk's entry to its own index, so an entry ends as the chunk's first
 // segment (num where no segment was kept).
-__device__ void plan_decode_one_wave(const PlanArgs& a, int32_t* tab_lds) {
+__device__ void plan_decode_one_wave(const PlanArgs& a, int32_t* lds) {
+  int32_t* const first_l = lds;
+  int32_t* const o_l = lds + 65;
+  int32_t* const t_l = lds + 130;
+  int32_t* const len_l = lds + 195;
+  int32_t* const tab_lds = lds + kOneWaveReqWords;
   int32_t* ws = a.ws;
   int32_t* req = ws + a.req_off;
   int4* items = reinterpret_cast<int4*>(ws + a.items_off);
@@ -110,23 +121,40 @@ __device__ void plan_decode_one_wave(const PlanArgs& a, int32_t* tab_lds) {
   }
   for (int cc = b; cc <= nchunks; cc += 64) tab_lds[cc] = num;
   if (on) {
-    if (t == 0) {  // an empty request keeps one empty segment
-      if (first < num) {
-        items[first] = make_int4(b, 0, 0, -1);
-        atomicMin(&tab_lds[o / C < nchunks ? o / C : nchunks - 1], first);
-      }
-    } else {
-      for (int sgi = 0; sgi < nseg && first + sgi < num; ++sgi) {
-        const int cc = o / C + sgi;
-        const int64_t g0 = o > (int64_t)cc * C ? o : (int64_t)cc * C;
-        const int64_t g1 = (int64_t)o + t < ((int64_t)cc + 1) * C ? (int64_t)o + t : ((int64_t)cc + 1) * C;
-        const int kb = (int)((g0 - o) * a.tile);
-        const int ke = (int)((g1 - o) * a.tile < L ? (g1 - o) * a.tile : L);
-        items[first + sgi] = make_int4(b, kb, ke, nseg > 1 ? first + sgi : -1);
-        atomicMin(&tab_lds[cc], first + sgi);
-      }
-    }
+    first_l[b] = first;
+    o_l[b] = o;
+    t_l[b] = t;
+    len_l[b] = L;
   }
+  if (b == 0) first_l[B] = total;
+  // other lanes read these entries: order the LDS writes before the reads
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // segment j belongs to the request r with first_l[r] <= j < first_l[r + 1]
+  // (every request has at least one segment, so the offsets increase)
+  for (int jseg = b; jseg < num; jseg += 64) {
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (first_l[mid] <= jseg) lo = mid; else hi = mid;
+    }
+    const int r = lo, ro = o_l[r], rt = t_l[r], rl = len_l[r];
+    const int sgi = jseg - first_l[r], rn = first_l[r + 1] - first_l[r];
+    if (rt == 0) {  // an empty request keeps one empty segment
+      items[jseg] = make_int4(r, 0, 0, -1);
+      atomicMin(&tab_lds[ro / C < nchunks ? ro / C : nchunks - 1], jseg);
+      continue;
+    }
+    const int cc = ro / C + sgi;
+    const int64_t g0 = ro > (int64_t)cc * C ? ro : (int64_t)cc * C;
+    const int64_t g1 = (int64_t)ro + rt < ((int64_t)cc + 1) * C ? (int64_t)ro + rt : ((int64_t)cc + 1) * C;
+    const int kb = (int)((g0 - ro) * a.tile);
+    const int ke = (int)((g1 - ro) * a.tile < rl ? (g1 - ro) * a.tile : rl);
+    items[jseg] = make_int4(r, kb, ke, rn > 1 ? jseg : -1);
+    atomicMin(&tab_lds[cc], jseg);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   for (int cc = b; cc <= nchunks; cc += 64) tab[cc] = cc == nchunks ? num : tab_lds[cc];
   if (b == 0) {
     ws[WS_MODE] = PKV_DECODE;

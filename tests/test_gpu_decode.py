@@ -225,18 +225,48 @@ def test_several_new_tokens_per_request(n, hq, hkv, kv_chunk):
     assert_lse_close(lse, rlse)
 
 
+def _merge_waves(capacity, batch):
+    """Waves per merge workgroup the library picks (decode_merge.h)."""
+    per = capacity // batch
+    return 8 if per >= 64 else (4 if per >= 16 else 1)
+
+
+@pytest.mark.parametrize("B,lens,hq,hkv,d,n,target,waves", [
+    (1, 60000, 16, 2, 128, 1, 512, 8),            # one long request: hundreds of splits
+    (1, 20000, 8, 8, 64, 3, 256, 8),              # head_dim 64, three new tokens
+    (5, [0, 30000, 2500, 1, 17000], 8, 1, 64, 1, 400, 8),  # one- and two-token requests beside long ones
+    (12, (4000, 12000), 32, 8, 128, 1, 256, 4),   # dozens of splits per request
+    (12, (4000, 12000), 32, 8, 128, 2, 256, 4),
+    (40, (1000, 3000), 32, 8, 128, 1, 256, 1),    # a few splits per request
+])
+def test_merge_of_many_splits(B, lens, hq, hkv, d, n, target, waves):
+    """Requests cut into many splits, so the merge runs its several-wave
+    two-pass form (or the one-pass form, last case): against the oracle."""
+    spec = Spec(f"merge{B}", "decode", B, hq, hkv, d, 16, lens, n)
+    hb = make_host_batch(spec, 70 + B + n)
+    units = hkv * -(-(n * (hq // hkv)) // 16)
+    o, lse, plan, _ = run_decode(hb, decode_q_len=n, split_target=target * units)
+    ws = plan.workspace.cpu().numpy().view(np.int32)
+    assert _merge_waves(int(ws[3]), B) == waves, (int(ws[3]), B)
+    ro, rlse = oracle_decode(hb)
+    assert_bf16_close(o, ro, spec.name)
+    assert_lse_close(lse, rlse)
+
+
 def test_plan_matches_oracle_rederivation_bit_for_bit():
     torch = torch_mod()
     pkv = _pkv()
     rng = np.random.default_rng(11)
     cases = ((0, 0, False), (0, 100, False), (64, 0, False), (0, 50000, False), (0, 0, True), (0, 300, True),
              (96, 0, True))
-    # 37 and 64 requests take the one-wave plan, 150 the workgroup one; the
-    # 64-request batch has a run of empty requests
-    for B, (kv_chunk, target, fp8) in [(B, c) for B in (37, 150) for c in cases] + [(64, cases[0]), (64, cases[4])]:
+    # up to 64 requests take the one-wave plan, 150 the workgroup one; the
+    # 64-request batch has a run of empty requests; one to three requests
+    # have more segments each than the wave has lanes
+    for B, (kv_chunk, target, fp8) in ([(B, c) for B in (37, 150) for c in cases] + [(64, cases[0]), (64, cases[4])] +
+                                       [(1, cases[0]), (1, cases[4]), (3, cases[0]), (2, cases[1])]):
         max_kv = 5000
         L = rng.integers(0, max_kv + 1, size=B).astype(np.int32)
-        L[5] = max_kv + 100  # clamped
+        L[min(5, B - 1)] = max_kv + 100  # clamped
         if B == 64:
             L[20:29] = 0
         extra = dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=64, q_block=1) if fp8 else {}
