@@ -71,8 +71,11 @@ __device__ __forceinline__ int wave_inclusive_scan32(int v) {
   return v;
 }
 
-// LDS words the one-wave decode plan keeps per batch ahead of its chunk table.
+// LDS words the one-wave decode plan keeps per batch ahead of its chunk table,
+// and the most segments per request for which each lane writes its own
+// request's segments (beyond it the segments are spread over the lanes).
 constexpr int kOneWaveReqWords = 4 * 65;
+constexpr int kOneWaveLaneSegs = 8;
 
 // Whether the one-wave decode plan below applies (decided on the host too).
 __host__ __device__ __forceinline__ bool plan_decode_by_one_wave(const PlanArgs& a) {
@@ -81,13 +84,14 @@ __host__ __device__ __forceinline__ bool plan_decode_by_one_wave(const PlanArgs&
 }
 
 // Balanced decode chunks for at most 64 requests, by one wave (one lane per
-// request for the scans, then the segments spread over all lanes; 32-bit
-// arithmetic, no workgroup barrier): the same work list, offsets and chunk
-// table as the workgroup path below.  LDS holds the requests' segment
-// offsets, tile offsets, tile counts and lengths (4 x 65 words) and then the
-// chunk table (nchunks + 1 <= capacity + 1 entries): every segment lowers its
-// chunk's entry to its own index, so an entry ends as the chunk's first
-// segment (num where no segment was kept).
+// request for the scans; the segments written by their request's lane, or
+// spread over all lanes when a request has many; 32-bit arithmetic, no
+// workgroup barrier): the same work list, offsets and chunk table as the
+// workgroup path below.  LDS holds the requests' segment offsets, tile
+// offsets, tile counts and lengths (4 x 65 words) and then the chunk table
+// (nchunks + 1 <= capacity + 1 entries): every segment lowers its chunk's
+// entry to its own index, so an entry ends as the chunk's first segment (num
+// where no segment was kept).
 __device__ void plan_decode_one_wave(const PlanArgs& a, int32_t* lds) {
   int32_t* const first_l = lds;
   int32_t* const o_l = lds + 65;
@@ -120,30 +124,12 @@ __device__ void plan_decode_one_wave(const PlanArgs& a, int32_t* lds) {
     req[B] = total;
   }
   for (int cc = b; cc <= nchunks; cc += 64) tab_lds[cc] = num;
-  if (on) {
-    first_l[b] = first;
-    o_l[b] = o;
-    t_l[b] = t;
-    len_l[b] = L;
-  }
-  if (b == 0) first_l[B] = total;
-  // other lanes read these entries: order the LDS writes before the reads
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  // segment j belongs to the request r with first_l[r] <= j < first_l[r + 1]
-  // (every request has at least one segment, so the offsets increase)
-  for (int jseg = b; jseg < num; jseg += 64) {
-    int lo = 0, hi = B;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (first_l[mid] <= jseg) lo = mid; else hi = mid;
-    }
-    const int r = lo, ro = o_l[r], rt = t_l[r], rl = len_l[r];
-    const int sgi = jseg - first_l[r], rn = first_l[r + 1] - first_l[r];
+  // segment sgi of request r: the item and its chunk-table entry
+  auto put = [&](int r, int ro, int rt, int rl, int rn, int sgi, int jseg) {
     if (rt == 0) {  // an empty request keeps one empty segment
       items[jseg] = make_int4(r, 0, 0, -1);
       atomicMin(&tab_lds[ro / C < nchunks ? ro / C : nchunks - 1], jseg);
-      continue;
+      return;
     }
     const int cc = ro / C + sgi;
     const int64_t g0 = ro > (int64_t)cc * C ? ro : (int64_t)cc * C;
@@ -152,6 +138,37 @@ __device__ void plan_decode_one_wave(const PlanArgs& a, int32_t* lds) {
     const int ke = (int)((g1 - ro) * a.tile < rl ? (g1 - ro) * a.tile : rl);
     items[jseg] = make_int4(r, kb, ke, rn > 1 ? jseg : -1);
     atomicMin(&tab_lds[cc], jseg);
+  };
+  int most = nseg;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) most = max(most, __shfl_xor(most, off, 64));
+  if (most <= kOneWaveLaneSegs) {
+    // few segments per request: each lane writes its own request's
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    for (int sgi = 0; sgi < nseg && first + sgi < num; ++sgi) put(b, o, t, L, nseg, sgi, first + sgi);
+  } else {
+    // many (a few long requests): the segments spread over all lanes; segment
+    // j belongs to the request r with first_l[r] <= j < first_l[r + 1] (every
+    // request has at least one segment, so the offsets increase)
+    if (on) {
+      first_l[b] = first;
+      o_l[b] = o;
+      t_l[b] = t;
+      len_l[b] = L;
+    }
+    if (b == 0) first_l[B] = total;
+    // other lanes read these entries: order the LDS writes before the reads
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    for (int jseg = b; jseg < num; jseg += 64) {
+      int lo = 0, hi = B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (first_l[mid] <= jseg) lo = mid; else hi = mid;
+      }
+      put(lo, o_l[lo], t_l[lo], len_l[lo], first_l[lo + 1] - first_l[lo], jseg - first_l[lo], jseg);
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -262,6 +262,7 @@ def test_plan_matches_oracle_rederivation_bit_for_bit():
     # up to 64 requests take the one-wave plan, 150 the workgroup one; the
     # 64-request batch has a run of empty requests; one to three requests
     # have more segments each than the wave has lanes
+    modes = set()
     for B, (kv_chunk, target, fp8) in ([(B, c) for B in (37, 150) for c in cases] + [(64, cases[0]), (64, cases[4])] +
                                        [(1, cases[0]), (1, cases[4]), (3, cases[0]), (2, cases[1])]):
         max_kv = 5000
@@ -287,10 +288,13 @@ def test_plan_matches_oracle_rederivation_bit_for_bit():
         assert np.array_equal(items, ref["items"])
         assert np.array_equal(ws[16:16 + B + 1], ref["split_off"])
         assert ws[6] == ref["nchunks"]
+        if B <= 64 and not kv_chunk:  # the one-wave plan: per-lane or spread segment writing
+            modes.add(int(np.diff(ref["split_off"]).max()) > 8)
         if kv_chunk:
             assert ws[7] == 0  # identity: one split per chunk
         else:
             assert np.array_equal(ws[ws[7]:ws[7] + ws[6] + 1], ref["chunk_tab"])
+    assert modes == {False, True}  # both ways of writing the segments ran
 
 
 @pytest.mark.parametrize("hkv,d", [(4, 128), (40, 128), (2, 64), (1, 64)])
