@@ -50,6 +50,7 @@ KERNEL_SOURCES = {
     "decode_n4_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "long_decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
+    "single_decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "decode_fp8": ["decode_fp8.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "extend_bf16": ["extend_bf16.hip", "lds_dma.h", "plan.hip", "device_common.h"],
     "extend_fp8": ["extend_fp8.hip", "lds_dma.h", "plan.hip", "device_common.h"],
@@ -85,6 +86,7 @@ def traffic_from_counters(workload: str):
 CALL_KERNELS = {
     "decode_bf16": ("decode_bf16_kernel", "decode_merge"),
     "long_decode_bf16": ("decode_bf16_kernel", "decode_merge"),
+    "single_decode_bf16": ("decode_bf16_kernel", "decode_merge"),
     "decode_fp8": ("decode_fp8_kernel", "decode_merge"),
     "decode_n4_bf16": ("decode_bf16_kernel", "decode_merge"),
     "extend_bf16": ("extend_bf16_kernel",),
@@ -207,9 +209,10 @@ class DecodeRunner:
     def describe(self):
         s = self.spec
         lo, hi = s.prefix
+        cached = f"{lo}" if lo == hi else f"U[{lo},{hi}]"
         return {"workload": s.name, "batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
                 "head_dim": s.head_dim, "page_size": s.page_size,
-                "cached_len": f"U[{lo},{hi}] + {self.q_len} new token{'s' if self.q_len > 1 else ''}",
+                "cached_len": f"{cached} + {self.q_len} new token{'s' if self.q_len > 1 else ''}",
                 "kv_dtype": "fp8_e4m3" if self.fp8 else "bf16", "layers_per_step": self.layers,
                 "kv_bytes_per_layer": self.kv_bytes_per_layer}
 
@@ -388,12 +391,12 @@ class ExtendRunner:
                 "algorithmic_flops_per_launch": self.flops_per_layer, "avg_launch_us": round(avg_launch_s * 1e6, 2)}
 
 
-RUNNERS = {"decode_bf16": DecodeRunner, "long_decode_bf16": DecodeRunner, "decode_fp8": DecodeRunner,
+RUNNERS = {"decode_bf16": DecodeRunner, "long_decode_bf16": DecodeRunner, "single_decode_bf16": DecodeRunner, "decode_fp8": DecodeRunner,
            "decode_n4_bf16": DecodeRunner, "extend_bf16": ExtendRunner, "extend_fp8": ExtendRunner,
            "sparse_decode_bf16": SparseDecodeRunner, "sparse_decode_fp8": SparseDecodeRunner}
-UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "decode_fp8": "GB/s", "decode_n4_bf16": "GB/s",
+UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "single_decode_bf16": "GB/s", "decode_fp8": "GB/s", "decode_n4_bf16": "GB/s",
          "extend_bf16": "TFLOP/s", "extend_fp8": "TFLOP/s", "sparse_decode_bf16": "GB/s", "sparse_decode_fp8": "GB/s"}
-DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "decode_fp8": 4, "decode_n4_bf16": 4, "extend_bf16": 4,
+DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "single_decode_bf16": 4, "decode_fp8": 4, "decode_n4_bf16": 4, "extend_bf16": 4,
                   "extend_fp8": 4, "sparse_decode_bf16": 2, "sparse_decode_fp8": 2}
 
 
@@ -458,7 +461,7 @@ def main():
     ap.add_argument("--workload", default="decode_bf16", choices=sorted(RUNNERS))
     ap.add_argument("--layers", type=int, default=0, help="layers (distinct K/V pools) per step")
     ap.add_argument("--secondary", default="extend_bf16,long_decode_bf16,decode_fp8,decode_n4_bf16,extend_fp8,"
-                                           "sparse_decode_bf16,sparse_decode_fp8",
+                                           "sparse_decode_bf16,sparse_decode_fp8,single_decode_bf16",
                     help="comma list of workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -377,3 +377,8 @@ def test_full_size_decode_bf16_sampled():
 
 def test_full_size_long_decode_sampled():
     _sampled_full_size("long_decode_bf16", samples=6)
+
+
+def test_full_size_single_request_decode_sampled():
+    """One 131k-token request: its 256 splits go through the several-wave merge."""
+    _sampled_full_size("single_decode_bf16", samples=6)

@@ -19,6 +19,9 @@ name                   description
 ``extend_bf16``        16 requests, 32/8 heads, d=128, page 16, prefix
                        U[0,2048] cached, U[128,2048] new tokens
 ``long_decode_bf16``   B=8, 64/8 heads, d=128, page 64, cached U[32768,131072]
+``single_decode_bf16`` one request, 64/8 heads, d=128, page 64, 131071 cached
+                       tokens: every split of the device comes from one
+                       request, so the merge and the plan serve one row
 ``decode_fp8``         B=64, 32/8 heads, d=128, page 16, cached U[1024,8192];
                        E4M3 codes of N(0,1)/scale with per-64-token sfK,
                        per-(b,h) sfQ and per-channel sfV drawn from U[0.5,2]
@@ -82,6 +85,7 @@ SPECS = {
     "extend_bf16": Spec("extend_bf16", "extend", 16, 32, 8, 128, 16, (0, 2048), (128, 2048)),
     "long_decode_bf16": Spec("long_decode_bf16", "decode", 8, 64, 8, 128, 64,
                              (32768, 131072), 1),
+    "single_decode_bf16": Spec("single_decode_bf16", "decode", 1, 64, 8, 128, 64, (131071, 131071), 1),
     "decode_n4_bf16": Spec("decode_n4_bf16", "decode", 64, 32, 8, 128, 16, (512, 4096), 4),
     "extend_fp8": Spec("extend_fp8", "extend", 16, 32, 8, 128, 16, (0, 2048), (128, 2048), dtype="fp8",
                        k_block=16, q_block=1),
@@ -95,7 +99,8 @@ SPECS = {
 
 # Index used to derive the seed of each named workload (1000 + index).
 SPEC_INDEX = {"tiny_decode": 1, "tiny_extend": 1, "decode_bf16": 2, "extend_bf16": 3, "decode_n4_bf16": 6, "extend_fp8": 7,
-              "long_decode_bf16": 4, "decode_fp8": 5, "sparse_decode_bf16": 8, "sparse_decode_fp8": 10}
+              "long_decode_bf16": 4, "decode_fp8": 5, "sparse_decode_bf16": 8, "sparse_decode_fp8": 10,
+              "single_decode_bf16": 11}
 
 
 def seed_sequence(spec: Spec, seed: int) -> list:
