@@ -91,9 +91,15 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream():
+def _stream(t):
+    """The current stream of tensor t's device, as a raw handle.  torch's
+    accessor of the raw handle skips building a Stream object (about 2 us per
+    call); the public API serves where it is absent."""
     import torch
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(t.device.index)
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _need(t, name, dtype=None, ndim=None):
@@ -148,7 +154,7 @@ def plan_metadata(params: Params, mode: int, seq_lens, cu_seqlens_q=None, total_
     _need(workspace, "workspace")
     lib = load_library()
     _check(lib.pkv_plan_metadata(ctypes.byref(params), mode, batch, total_q, _ptr(seq_lens), _ptr(cu_seqlens_q),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(seq_lens)))
     return Plan(workspace, mode, batch, total_q, sc_bytes)
 
 
@@ -161,7 +167,7 @@ def kv_store(params: Params, k_pool, v_pool, k_new, v_new, slots):
         raise ValueError("k_new/v_new rows must match slots")
     lib = load_library()
     _check(lib.pkv_kv_store(ctypes.byref(params), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0], _ptr(k_new),
-                            _ptr(v_new), _ptr(slots), slots.shape[0], _stream()))
+                            _ptr(v_new), _ptr(slots), slots.shape[0], _stream(k_pool)))
 
 
 def block_sparse_table(params: Params, seq_lens, req_to_token, blk_indptr, blk_indices, block_size: int,
@@ -194,7 +200,7 @@ def block_sparse_table(params: Params, seq_lens, req_to_token, blk_indptr, blk_i
     _check(lib.pkv_block_sparse_table(ctypes.byref(params), B, _ptr(seq_lens), _ptr(req_to_token),
                                       req_to_token.shape[1], _ptr(req_pool_indices), _ptr(blk_indptr),
                                       _ptr(blk_indices), blk_indices.shape[0], int(block_size), _ptr(sfk),
-                                      _ptr(sparse_rtt), _ptr(sparse_lens), _ptr(sparse_sfk), _stream()))
+                                      _ptr(sparse_rtt), _ptr(sparse_lens), _ptr(sparse_sfk), _stream(seq_lens)))
     return sparse_rtt, sparse_lens, sparse_sfk
 
 
@@ -240,7 +246,7 @@ def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan:
                                k_pool.shape[0], _ptr(req_to_token), req_to_token.shape[1], _ptr(req_pool_indices),
                                _ptr(seq_lens), B, float(sm_scale), _ptr(sfq), _ptr(sfk), _ptr(sfv), _ptr(v_mean),
                                _ptr(ws), ws.numel() * ws.element_size(), _ptr(scratch),
-                               scratch.numel() * scratch.element_size(), _stream()))
+                               scratch.numel() * scratch.element_size(), _stream(q)))
     return out
 
 
@@ -286,5 +292,5 @@ def attn_extend(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, cu_se
                                k_pool.shape[0], _ptr(req_to_token), req_to_token.shape[1], _ptr(req_pool_indices),
                                _ptr(seq_lens), _ptr(cu_seqlens_q), B, total_q, float(sm_scale), _ptr(sfq),
                                _ptr(sfk), _ptr(sfv), _ptr(v_mean), _ptr(ws), ws.numel() * ws.element_size(),
-                               None, 0, _stream()))
+                               None, 0, _stream(q)))
     return out
