@@ -38,6 +38,10 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
   the request cut at that row's causal limit; unit scales and P
   unquantised equal ``paged_attention``; q8 = 0 gives sfV·mean(V8) over the
   visible keys).  Same running-max caveat as ``sage_decode``.
+* INT8 Q/K (``qk_codes="int8"`` of the three 8-bit functions): pinned by a
+  hand-worked two-key example with negative and extreme codes, equality with
+  the E4M3 reading where the integer codes' values are exact E4M3 values,
+  and the integer dot product (sign, range) against exact integer arithmetic.
 * ``plan_decode`` / ``plan_extend``: the split heuristic is a design choice,
   not from the pages; pinned by invariants (every token covered once, in
   order; bounds on tile multiples; capacity; the chunk is the smallest that
@@ -55,7 +59,7 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
 from .attention import paged_attention
 from .merge import lse_merge
 from .e4m3 import e4m3_encode, e4m3_decode, E4M3_MAX
-from .sage import sage_decode, sage_extend
+from .sage import sage_decode, sage_extend, qk_values
 from .plan import plan_decode, plan_extend, decode_target_items, DECODE_TILE, EXTEND_BLOCK_M
 from .kv_store import kv_store
 from .memory import score_matrix_bytes
@@ -63,7 +67,7 @@ from .block_sparse import block_sparse_decode, block_sparse_sage_decode
 
 __all__ = [
     "paged_attention", "lse_merge", "e4m3_encode",
-    "e4m3_decode", "E4M3_MAX", "sage_decode", "sage_extend", "plan_decode", "plan_extend",
+    "e4m3_decode", "E4M3_MAX", "sage_decode", "sage_extend", "qk_values", "plan_decode", "plan_extend",
     "DECODE_TILE", "EXTEND_BLOCK_M", "decode_target_items", "kv_store",
     "score_matrix_bytes", "block_sparse_decode", "block_sparse_sage_decode",
 ]

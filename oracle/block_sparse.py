@@ -29,6 +29,7 @@ from typing import Optional
 import numpy as np
 
 from .e4m3 import e4m3_decode, e4m3_encode
+from .sage import qk_values
 
 
 def key_mask(L: int, blocks, block_size: int) -> np.ndarray:
@@ -80,11 +81,13 @@ def block_sparse_decode(q, k_pool, v_pool, req_to_token, seq_lens, blk_indptr, b
 
 def block_sparse_sage_decode(q8, k8_pool, v8_pool, req_to_token, seq_lens, blk_indptr, blk_indices,
                              block_size: int, sfq, sfk, sfv, k_block: int, sm_scale: Optional[float] = None,
-                             v_mean=None, quantize_p: bool = True, req_pool_indices=None):
+                             v_mean=None, quantize_p: bool = True, req_pool_indices=None,
+                             qk_codes: str = "e4m3"):
     """The 8-bit formula of [FlashInfer-Sage] (README block) over the selected
     blocks: S = sm_scale·sfQ[b,h]·sfK[b,g,⌊j/k_block⌋]·(q8·k8_j) on listed keys,
     m the row max over them, P8 = E4M3(448·e^{S-m}), l = Σ e^{S-m} (unquantised),
-    O = sfV·(Σ P8_j·v8_j)/(448·l) (+ v_mean).  Same shapes as ``sage_decode``.
+    O = sfV·(Σ P8_j·v8_j)/(448·l) (+ v_mean).  Same shapes and ``qk_codes``
+    as ``sage_decode``.
     """
     q8 = np.asarray(q8)
     B, Hq, d = q8.shape
@@ -103,12 +106,12 @@ def block_sparse_sage_decode(q8, k8_pool, v8_pool, req_to_token, seq_lens, blk_i
                 out[b] = np.repeat(np.asarray(v_mean[b], np.float64), G, axis=0)
             continue
         slots = np.asarray(req_to_token[row, :L], np.int64)
-        K = e4m3_decode(np.asarray(k8_pool)[slots])
+        K = qk_values(np.asarray(k8_pool)[slots], qk_codes)
         V = e4m3_decode(np.asarray(v8_pool)[slots])
         kblk = np.arange(L) // k_block
         for h in range(Hq):
             g = h // G
-            dots = K[:, g, :] @ e4m3_decode(q8[b, h])
+            dots = K[:, g, :] @ qk_values(q8[b, h], qk_codes)
             S = sm_scale * float(sfq[b, h]) * np.asarray(sfk[b, g, kblk], np.float64) * dots
             S = np.where(keep, S, -np.inf)
             m = S.max()

@@ -24,6 +24,10 @@ Readings where the pages are silent or at odds:
   [B, Hkv, nblk]; decode has one query row per request so sfQ is [B, Hq];
   sfV and v_mean are [B, Hkv, d].
 * E4M3 is the OCP E4M3FN variant (largest finite value 448).
+* INT8 Q and K ([FlashInfer-Sage], code §3 and §4: Q/K may be INT8, whose
+  scores accumulate in 32-bit and enter the softmax as fp32): the same
+  formula with Q8 and K8 read as two's-complement integers (``qk_codes=
+  "int8"``).  The pages name INT8 for Q and K only, so V8 and P8 stay E4M3.
 """
 from __future__ import annotations
 
@@ -35,10 +39,26 @@ import numpy as np
 from .e4m3 import e4m3_decode, e4m3_encode
 
 
+def qk_values(codes, qk_codes: str = "e4m3"):
+    """Exact float64 values of Q or K codes: E4M3 bytes, or two's-complement
+    int8 ([FlashInfer-Sage], code §3) for ``qk_codes="int8"``."""
+    c = np.asarray(codes)
+    if qk_codes == "e4m3":
+        return e4m3_decode(c)
+    if qk_codes != "int8":
+        raise ValueError(f"qk_codes must be 'e4m3' or 'int8', got {qk_codes!r}")
+    if c.dtype == np.uint8:
+        c = c.view(np.int8)
+    if c.dtype != np.int8:
+        raise ValueError("int8 codes must be an int8 or uint8 array")
+    return c.astype(np.float64)
+
+
 def sage_decode(q8, k8_pool, v8_pool, req_to_token, seq_lens, sfq, sfk, sfv,
                 k_block: int, sm_scale: Optional[float] = None, v_mean=None,
-                quantize_p: bool = True, req_pool_indices=None):
+                quantize_p: bool = True, req_pool_indices=None, qk_codes: str = "e4m3"):
     """One query row per request. q8: [B, Hq, d] uint8 codes; pools [slots, Hkv, d].
+    ``qk_codes``: how q8 and the K pool's bytes read ("e4m3" or "int8").
 
     Returns (o [B, Hq, d] float64, lse [B, Hq] float64) with lse = m + ln l in
     the (scaled) S domain.  ``quantize_p=False`` keeps 448·p unrounded.
@@ -59,13 +79,13 @@ def sage_decode(q8, k8_pool, v8_pool, req_to_token, seq_lens, sfq, sfk, sfv,
                 out[b] = np.repeat(np.asarray(v_mean[b], np.float64), G, axis=0)
             continue
         slots = np.asarray(req_to_token[row, :L], dtype=np.int64)
-        K = e4m3_decode(np.asarray(k8_pool)[slots])  # [L, Hkv, d] exact
+        K = qk_values(np.asarray(k8_pool)[slots], qk_codes)  # [L, Hkv, d] exact
         V = e4m3_decode(np.asarray(v8_pool)[slots])
         blk = np.arange(L) // k_block
         for h in range(Hq):
             g = h // G
-            qv = e4m3_decode(q8[b, h])  # [d]
-            dots = K[:, g, :] @ qv  # exact in fp64 (products of 4-bit significands)
+            qv = qk_values(q8[b, h], qk_codes)  # [d]
+            dots = K[:, g, :] @ qv  # exact in fp64 (4-bit significands, or integers below 2^22)
             S = sm_scale * float(sfq[b, h]) * np.asarray(sfk[b, g, blk], np.float64) * dots
             m = S.max()
             p = np.exp(S - m)
@@ -84,7 +104,7 @@ def sage_decode(q8, k8_pool, v8_pool, req_to_token, seq_lens, sfq, sfk, sfv,
 
 def sage_extend(q8, k8_pool, v8_pool, req_to_token, seq_lens, cu_seqlens_q, sfq, sfk, sfv,
                 k_block: int, sm_scale: Optional[float] = None, v_mean=None,
-                quantize_p: bool = True, req_pool_indices=None):
+                quantize_p: bool = True, req_pool_indices=None, qk_codes: str = "e4m3"):
     """The same 8-bit formula for the new-token rows of an extend batch.
 
     q8: [T, Hq, d] codes, rows request-major (cu_seqlens_q); sfq: [T, Hq] (one
@@ -109,14 +129,14 @@ def sage_extend(q8, k8_pool, v8_pool, req_to_token, seq_lens, cu_seqlens_q, sfq,
         L = int(seq_lens[b])
         p0 = L - (q1 - q0)
         slots = np.asarray(req_to_token[row, :L], dtype=np.int64)
-        K = e4m3_decode(np.asarray(k8_pool)[slots])  # [L, Hkv, d] exact
+        K = qk_values(np.asarray(k8_pool)[slots], qk_codes)  # [L, Hkv, d] exact
         V = e4m3_decode(np.asarray(v8_pool)[slots])
         blk = np.arange(L) // k_block
         for t in range(q0, q1):
             vis = p0 + (t - q0) + 1  # keys 0 .. p_b + i
             for h in range(Hq):
                 g = h // G
-                dots = K[:vis, g, :] @ e4m3_decode(q8[t, h])
+                dots = K[:vis, g, :] @ qk_values(q8[t, h], qk_codes)
                 S = sm_scale * float(sfq[t, h]) * np.asarray(sfk[b, g, blk[:vis]], np.float64) * dots
                 m = S.max()
                 p = np.exp(S - m)

@@ -67,7 +67,7 @@ class Spec:
     page_size: int
     prefix: LenSpec
     new: LenSpec
-    dtype: str = "bf16"  # "fp32" (host-only tiny case), "bf16" or "fp8"
+    dtype: str = "bf16"  # "fp32" (host-only tiny case), "bf16", "fp8" or "int8" (Sage INT8 Q/K, E4M3 V)
     pool: Union[str, int] = "2x"
     k_block: int = 64  # fp8: tokens per sfK block
     q_block: int = 1  # fp8: q rows per sfQ block
@@ -244,7 +244,9 @@ class HostBatch:
     ``k_pool``/``v_pool`` hold every referenced row *including* the new tokens
     (the state after ``kv_store``); ``k_new``/``v_new`` are those new rows, in
     ``new_slots`` order.  Unreferenced rows are NaN when ``poison`` was set.
-    fp8 batches carry E4M3 codes (uint8) in ``*_codes`` and the scales.
+    fp8 batches carry E4M3 codes (uint8) in ``*_codes`` and the scales;
+    int8 batches carry int8 codes of Q and K (scales U[lo, hi] / INT8_LEVELS,
+    so code·scale is about N(0,1)) and E4M3 codes of V.
     """
 
     layout: Layout
@@ -263,6 +265,15 @@ class HostBatch:
     sfv: Optional[np.ndarray] = None  # [B, Hkv, d] float32
 
 
+# int8 Sage codes: code = clip(rint(x / sf), -127, 127) with sf = U[lo, hi] /
+# INT8_LEVELS, i.e. a standard normal x spans about +-4 * 16 / U codes.
+INT8_LEVELS = 16.0
+
+
+def int8_codes(x: np.ndarray) -> np.ndarray:
+    return np.clip(np.rint(x), -127, 127).astype(np.int8)
+
+
 def make_host_batch(spec: Spec, seed: int = 0, poison: bool = True,
                     stride: Optional[int] = None) -> HostBatch:
     """Draw a complete batch on the host (small and medium sizes).
@@ -279,7 +290,8 @@ def make_host_batch(spec: Spec, seed: int = 0, poison: bool = True,
     if spec.dtype == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
     hb = HostBatch(layout=lay, q=q, k_pool=k, v_pool=v, k_new=None, v_new=None)
-    if spec.dtype == "fp8":
+    if spec.dtype in ("fp8", "int8"):
+        i8 = spec.dtype == "int8"
         B = spec.batch
         lo, hi = spec.scale_range
         nblk = max((lay.max_kv_len + spec.k_block - 1) // spec.k_block, 1)
@@ -288,15 +300,19 @@ def make_host_batch(spec: Spec, seed: int = 0, poison: bool = True,
         sfq = rng.uniform(lo, hi, size=(T if spec.mode == "extend" else B, Hq)).astype(np.float32)
         sfk = rng.uniform(lo, hi, size=(B, Hkv, nblk)).astype(np.float32)
         sfv = rng.uniform(lo, hi, size=(B, Hkv, d)).astype(np.float32)
+        if i8:
+            sfq = (sfq / INT8_LEVELS).astype(np.float32)
+            sfk = (sfk / INT8_LEVELS).astype(np.float32)
+        qk_codes = int8_codes if i8 else e4m3_codes
         req_of_row = np.repeat(np.arange(B), lay.new_lens)
-        q_codes = e4m3_codes(q / (sfq if spec.mode == "extend" else sfq[req_of_row])[:, :, None])
+        q_codes = qk_codes(q / (sfq if spec.mode == "extend" else sfq[req_of_row])[:, :, None])
         owner = np.where(used, lay.slot_owner, 0)
         blk = np.where(used, lay.slot_pos, 0) // spec.k_block
         ks = sfk[owner, :, blk]  # [S, Hkv]
         vs = sfv[owner]  # [S, Hkv, d]
-        k_codes = e4m3_codes(k / ks[:, :, None])
+        k_codes = qk_codes(k / ks[:, :, None])
         v_codes = e4m3_codes(v / vs)
-        k_codes[~used] = 0x7F  # E4M3 NaN in unreferenced rows
+        k_codes[~used] = -128 if i8 else 0x7F  # extreme int8 / E4M3 NaN in unreferenced rows
         v_codes[~used] = 0x7F
         hb.q_codes, hb.k_codes, hb.v_codes = q_codes, k_codes, v_codes
         hb.sfq, hb.sfk, hb.sfv = sfq, sfk, sfv
@@ -374,7 +390,8 @@ def make_device_batch(spec: Spec, seed: int = 0, device="cuda", layers: int = 1,
 
     Draw order on the device: Q, then per layer the K pool and the V pool;
     for fp8 the scales are drawn first on the host (U[lo, hi]) and the codes
-    are E4M3 casts of N(0,1)/scale.
+    are E4M3 casts of N(0,1)/scale; for int8 the Q and K scales are divided by
+    INT8_LEVELS and their codes are clip(rint(N(0,1)/scale), -127, 127).
     """
     import torch
     lay, rng = make_layout(spec, seed, stride=stride)
@@ -390,13 +407,22 @@ def make_device_batch(spec: Spec, seed: int = 0, device="cuda", layers: int = 1,
                      cu_seqlens_q=i32(lay.cu_seqlens_q), new_slots=new_slots)
     if lay.blk_indptr is not None:
         db.blk_indptr, db.blk_indices = i32(lay.blk_indptr), i32(lay.blk_indices)
-    if spec.dtype == "fp8":
+    if spec.dtype in ("fp8", "int8"):
+        i8 = spec.dtype == "int8"
         B = spec.batch
         lo, hi = spec.scale_range
         nblk = max((lay.max_kv_len + spec.k_block - 1) // spec.k_block, 1)
         sfq = rng.uniform(lo, hi, size=(T if spec.mode == "extend" else B, Hq)).astype(np.float32)
         sfk = rng.uniform(lo, hi, size=(B, Hkv, nblk)).astype(np.float32)
         sfv = rng.uniform(lo, hi, size=(B, Hkv, d)).astype(np.float32)
+        if i8:
+            sfq = (sfq / INT8_LEVELS).astype(np.float32)
+            sfk = (sfk / INT8_LEVELS).astype(np.float32)
+
+        def qk_cast(x):
+            if i8:
+                return torch.clamp(torch.round(x), -127, 127).to(torch.int8)
+            return x.to(torch.float8_e4m3fn).view(torch.uint8)
         db.sfq, db.sfk, db.sfv = (torch.from_numpy(x).to(dev) for x in (sfq, sfk, sfv))
         used = lay.slot_owner >= 0
         owner = torch.from_numpy(np.where(used, lay.slot_owner, 0).astype(np.int64)).to(dev)
@@ -406,10 +432,10 @@ def make_device_batch(spec: Spec, seed: int = 0, device="cuda", layers: int = 1,
         req_of_row = torch.from_numpy(np.repeat(np.arange(B), lay.new_lens)).to(dev)
         qf = torch.randn((T, Hq, d), generator=g, device=dev, dtype=torch.float32)
         q_scale = db.sfq if spec.mode == "extend" else db.sfq[req_of_row]
-        db.q = (qf / q_scale[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        db.q = qk_cast(qf / q_scale[:, :, None])
         for _ in range(layers):
             kf = torch.randn((S, Hkv, d), generator=g, device=dev, dtype=torch.float32)
-            kc = (kf / k_scale[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+            kc = qk_cast(kf / k_scale[:, :, None])
             del kf
             vf = torch.randn((S, Hkv, d), generator=g, device=dev, dtype=torch.float32)
             vc = (vf / v_scale).to(torch.float8_e4m3fn).view(torch.uint8)
