@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
-PKV_BF16, PKV_FP8_E4M3 = 0, 1
+PKV_BF16, PKV_FP8_E4M3, PKV_SAGE_INT8 = 0, 1, 2
 PKV_DECODE, PKV_EXTEND = 0, 1
 
 EXPORTED = ("pkv_workspace_size", "pkv_plan_metadata", "pkv_kv_store", "pkv_block_sparse_table",
@@ -115,10 +115,14 @@ def _need(t, name, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
+def _is_8bit(params: Params) -> bool:
+    return params.kv_dtype in (PKV_FP8_E4M3, PKV_SAGE_INT8)
+
+
 def _need_rows(t, name, params: Params):
     """K/V pools and new rows: [n, Hkv, d] of the params' element type."""
     _need(t, name, ndim=3)
-    esize = 1 if params.kv_dtype == PKV_FP8_E4M3 else 2
+    esize = 1 if _is_8bit(params) else 2
     if tuple(t.shape[1:]) != (params.num_kv_heads, params.head_dim) or t.element_size() != esize:
         raise ValueError(f"{name} must be [n, {params.num_kv_heads}, {params.head_dim}] with {esize}-byte elements, "
                          f"got {tuple(t.shape)} with {t.element_size()}-byte elements")
@@ -177,7 +181,7 @@ def block_sparse_table(params: Params, seq_lens, req_to_token, blk_indptr, blk_i
     [B, max_kv_len], sparse_seq_lens [B], sparse_sfk or None); pass them to
     plan_metadata / attn_decode in place of req_to_token, seq_lens and sfk."""
     import torch
-    fp8 = params.kv_dtype == PKV_FP8_E4M3
+    fp8 = _is_8bit(params)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     _need(req_to_token, "req_to_token", torch.int32, 2)
     _need(blk_indptr, "blk_indptr", torch.int32, 1)
@@ -207,9 +211,11 @@ def block_sparse_table(params: Params, seq_lens, req_to_token, blk_indptr, blk_i
 def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan: Plan, scratch=None,
                 out=None, lse=None, sm_scale: Optional[float] = None, req_pool_indices=None,
                 sfq=None, sfk=None, sfv=None, v_mean=None):
-    """Decode attention: q [B, Hq, d] (bf16, or uint8 E4M3 codes) -> out [B, Hq, d] bf16."""
+    """Decode attention: q [B, Hq, d] (bf16, uint8 E4M3 codes, or int8 codes for PKV_SAGE_INT8)
+    -> out [B, Hq, d] bf16."""
     import torch
-    _need(q, "q", torch.uint8 if params.kv_dtype == PKV_FP8_E4M3 else torch.bfloat16, 3)
+    qt = {PKV_FP8_E4M3: torch.uint8, PKV_SAGE_INT8: torch.int8}.get(params.kv_dtype, torch.bfloat16)
+    _need(q, "q", qt, 3)
     _need_rows(k_pool, "k_pool", params)
     _need_rows(v_pool, "v_pool", params)
     _need(req_to_token, "req_to_token", torch.int32, 2)
@@ -223,7 +229,7 @@ def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan:
     n = max(params.decode_q_len, 1)
     if q.shape[0] != B * n:
         raise ValueError(f"q must have batch * decode_q_len = {B * n} rows")
-    if params.kv_dtype == PKV_FP8_E4M3 and sfk is not None:
+    if _is_8bit(params) and sfk is not None:
         nblk = -(-params.max_kv_len // params.k_block)
         if tuple(sfk.shape) != (B, params.num_kv_heads, nblk):
             raise ValueError(f"sfk must be [B, Hkv, ceil(max_kv_len/k_block)] = {(B, params.num_kv_heads, nblk)}")

@@ -21,6 +21,11 @@
 //  * Oᵀ += V8ᵀ·P8ᵀ: each lane gathers 16 keys x 8 channels of V8 and
 //    transposes the bytes with permutes into 8 A operands; 64 of the 128
 //    k slots carry the tile's keys, the rest are zero.
+// With INT8 Q and K (the page's code §3 and §4) Sᵀ is two int8 MFMAs
+// 16x16x64 per 16 keys, one per 16-byte half of the lanes' 32 bytes; A and
+// B take the same bytes of the same lanes, so their products pair channel
+// with channel whatever order the instruction sums them in.  The int32 dot
+// product (|q·k| <= 128·128·128 < 2^24) converts to fp32 exactly.
 #include "decode_stream.h"
 #include "device_common.h"
 #include "pkv_internal.h"
@@ -34,6 +39,22 @@ constexpr int kTile8 = 64;
 __device__ __forceinline__ floatx4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, floatx4 c) {
   // fp8 E4M3 for both operands (format 0), block scales 2^0 (E8M0 127)
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Scores of 16 keys x 16 columns over the 128 channels: E4M3 codes, or
+// int8 codes (two int8 MFMAs over the lanes' two 16-byte halves).
+template <bool I8>
+__device__ __forceinline__ floatx4 qk_scores(i32x8 kop, i32x8 qop) {
+  if constexpr (I8) {
+    const i32x4 k0 = {kop[0], kop[1], kop[2], kop[3]}, k1 = {kop[4], kop[5], kop[6], kop[7]};
+    const i32x4 q0 = {qop[0], qop[1], qop[2], qop[3]}, q1 = {qop[4], qop[5], qop[6], qop[7]};
+    i32x4 s = {0, 0, 0, 0};
+    s = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, q0, s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, q1, s, 0, 0, 0);
+    return floatx4{(float)s[0], (float)s[1], (float)s[2], (float)s[3]};
+  } else {
+    return mfma_fp8_16x16x128(kop, qop, floatx4{0.f, 0.f, 0.f, 0.f});
+  }
 }
 
 struct Tile8 {
@@ -178,7 +199,7 @@ __device__ __forceinline__ void finish_empty8(const DecodeArgs& a, SegWindow& w,
 // tiles belong to.
 // MULTI: several new tokens per request (per-lane causal limits); the
 // one-token instance keeps none of that state in the tile loop.
-template <bool MULTI>
+template <bool MULTI, bool I8>
 __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, int s1, int unit, int4* win_rec,
                                                  int2* win_req) {
   constexpr int D = 128;
@@ -222,8 +243,7 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
     for (int blk = 0; blk < 4; ++blk) {
       const i32x8 kop = {(int)cur.k[blk][0][0], (int)cur.k[blk][0][1], (int)cur.k[blk][0][2], (int)cur.k[blk][0][3],
                          (int)cur.k[blk][1][0], (int)cur.k[blk][1][1], (int)cur.k[blk][1][2], (int)cur.k[blk][1][3]};
-      floatx4 s = {0.f, 0.f, 0.f, 0.f};
-      s = mfma_fp8_16x16x128(kop, qop, s);
+      const floatx4 s = qk_scores<I8>(kop, qop);
       const int tb = t0 + 16 * blk;
       const float ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cur.ks), blk)) * qscale;
 #pragma unroll
@@ -318,7 +338,7 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
 }
 
 // WPB units of one chunk per workgroup, as in the bf16 decode.
-template <int WPB, bool MULTI>
+template <int WPB, bool MULTI, bool I8>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_fp8_kernel(DecodeArgs a) {
   const int32_t* __restrict__ ws = a.ws;
   // 1-D grid, unit group fastest: the workgroups of one chunk are
@@ -333,31 +353,44 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
   const int s0 = tab ? ws[tab + c] : c, s1 = tab ? ws[tab + c + 1] : c + 1;
   __shared__ int4 win_rec[WPB][64];
   __shared__ int2 win_req[WPB][64];
-  decode_fp8_chunk<MULTI>(a, s0, s1, unit, win_rec[wv], win_req[wv]);
+  decode_fp8_chunk<MULTI, I8>(a, s0, s1, unit, win_rec[wv], win_req[wv]);
 }
 
-hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch, hipStream_t s) {
-  (void)head_dim;  // 128 only (validated by the host API)
+template <bool MULTI, bool I8>
+void launch_decode_fp8_as(const DecodeArgs& a, dim3 grid, int wpb, hipStream_t s) {
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * wpb), 0, s, a); };
+  if (wpb == 8) go(decode_fp8_kernel<8, MULTI, I8>);
+  else if (wpb == 4) go(decode_fp8_kernel<4, MULTI, I8>);
+  else if (wpb == 2) go(decode_fp8_kernel<2, MULTI, I8>);
+  else go(decode_fp8_kernel<1, MULTI, I8>);
+}
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, bool qk_int8, int64_t capacity, int32_t batch, hipStream_t s) {
+  // head_dim 128 only (validated by the host API)
   if (capacity <= 0 || batch <= 0) return hipSuccess;
   const int units = a.hkv * a.head_groups;
   const int wpb = decode_waves_per_block(units);
-  dim3 grid((unsigned)(capacity * ceil_div(units, wpb)));
-  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * wpb), 0, s, a); };
+  const dim3 grid((unsigned)(capacity * ceil_div(units, wpb)));
   if (a.q_len > 1) {
-    if (wpb == 8) go(decode_fp8_kernel<8, true>); else if (wpb == 4) go(decode_fp8_kernel<4, true>);
-    else if (wpb == 2) go(decode_fp8_kernel<2, true>); else go(decode_fp8_kernel<1, true>);
+    if (qk_int8) launch_decode_fp8_as<true, true>(a, grid, wpb, s);
+    else launch_decode_fp8_as<true, false>(a, grid, wpb, s);
   } else {
-    if (wpb == 8) go(decode_fp8_kernel<8, false>); else if (wpb == 4) go(decode_fp8_kernel<4, false>);
-    else if (wpb == 2) go(decode_fp8_kernel<2, false>); else go(decode_fp8_kernel<1, false>);
+    if (qk_int8) launch_decode_fp8_as<false, true>(a, grid, wpb, s);
+    else launch_decode_fp8_as<false, false>(a, grid, wpb, s);
   }
   return hipGetLastError();
 }
 
-hipError_t decode_fp8_resident_items(int units, int64_t* items) {
+template <bool I8>
+const void* decode_fp8_kernel_for(int wpb) {
+  return wpb == 8 ? (const void*)decode_fp8_kernel<8, false, I8> : wpb == 4 ? (const void*)decode_fp8_kernel<4, false, I8>
+       : wpb == 2 ? (const void*)decode_fp8_kernel<2, false, I8> : (const void*)decode_fp8_kernel<1, false, I8>;
+}
+
+hipError_t decode_fp8_resident_items(int units, bool qk_int8, int64_t* items) {
   const int wpb = decode_waves_per_block(units);
-  const void* k = wpb == 8 ? (const void*)decode_fp8_kernel<8, false> : wpb == 4 ? (const void*)decode_fp8_kernel<4, false>
-                : wpb == 2 ? (const void*)decode_fp8_kernel<2, false> : (const void*)decode_fp8_kernel<1, false>;
-  return resident_items_of(k, wpb, units, items);
+  return resident_items_of(qk_int8 ? decode_fp8_kernel_for<true>(wpb) : decode_fp8_kernel_for<false>(wpb), wpb, units,
+                           items);
 }
 
 }  // namespace pkv

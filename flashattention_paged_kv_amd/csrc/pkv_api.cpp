@@ -62,8 +62,11 @@ int check_params(const pkv_params* p, int mode) {
     // inapplicable plan input (FlashInfer Sage page, code §2)
     if (p->q_block != 0) return fail(PKV_EINVAL, "q_block is unsupported by a bf16 plan");
     if (p->k_block != 0) return fail(PKV_EINVAL, "k_block is unsupported by a bf16 plan");
-  } else if (p->kv_dtype == PKV_FP8_E4M3) {
-    if (p->head_dim != 128) return fail(PKV_EUNSUPPORTED, "kv_dtype=fp8_e4m3 requires head_dim=128");
+  } else if (pkv::is_8bit(*p)) {
+    const char* name = p->kv_dtype == PKV_FP8_E4M3 ? "fp8_e4m3" : "sage_int8";
+    if (p->head_dim != 128) return fail(PKV_EUNSUPPORTED, "kv_dtype=%s requires head_dim=128", name);
+    if (p->kv_dtype == PKV_SAGE_INT8 && mode != PKV_DECODE)
+      return fail(PKV_EUNSUPPORTED, "kv_dtype=sage_int8 is a DECODE path (INT8 Q/K decode of the Sage page)");
     if (p->k_block < 16 || p->k_block % 16 != 0)
       return fail(PKV_EINVAL, "k_block=%d must be a positive multiple of 16", p->k_block);
     if (p->q_block < 1) return fail(PKV_EINVAL, "q_block=%d must be >= 1", p->q_block);
@@ -78,7 +81,7 @@ int check_params(const pkv_params* p, int mode) {
   return PKV_OK;
 }
 
-int64_t elem_bytes(const pkv_params* p) { return p->kv_dtype == PKV_FP8_E4M3 ? 1 : 2; }
+int64_t elem_bytes(const pkv_params* p) { return pkv::is_8bit(*p) ? 1 : 2; }
 
 // Decode items the current device holds at once for these params (cached per
 // device and kernel variant).  Without a device (host-only sizing) the
@@ -102,7 +105,7 @@ int64_t resident_items(const pkv_params& p) {
     if (it != cache.end()) return it->second;
   }
   int64_t items = 0;
-  hipError_t e = p.kv_dtype == PKV_FP8_E4M3 ? pkv::decode_fp8_resident_items(units, &items)
+  hipError_t e = pkv::is_8bit(p) ? pkv::decode_fp8_resident_items(units, p.kv_dtype == PKV_SAGE_INT8, &items)
                                              : pkv::decode_bf16_resident_items(p.head_dim, units, &items);
   if (e != hipSuccess || items < 1) {
     (void)hipGetLastError();
@@ -200,11 +203,11 @@ int pkv_block_sparse_table(const pkv_params* params, int32_t batch, const int32_
     return fail(PKV_EINVAL, "num_indices=%lld must be in [0, 2^31)", (long long)num_indices);
   if (rtt_stride < params->max_kv_len)
     return fail(PKV_EINVAL, "rtt_stride=%lld is smaller than max_kv_len=%d", (long long)rtt_stride, params->max_kv_len);
-  const bool fp8 = params->kv_dtype == PKV_FP8_E4M3;
+  const bool fp8 = pkv::is_8bit(*params);
   if (fp8) {
     if (block_size % params->k_block != 0)
       return fail(PKV_EINVAL, "block_size=%d must be a multiple of k_block=%d", block_size, params->k_block);
-    if (batch > 0 && (!sfk || !sparse_sfk)) return fail(PKV_EINVAL, "the fp8_e4m3 path needs sfk and sparse_sfk");
+    if (batch > 0 && (!sfk || !sparse_sfk)) return fail(PKV_EINVAL, "the 8-bit path needs sfk and sparse_sfk");
   } else if (sfk || sparse_sfk) {
     return fail(PKV_EINVAL, "sfk and sparse_sfk are unsupported by a bf16 plan");
   }
@@ -265,14 +268,14 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
   if (rtt_stride < params->max_kv_len)
     return fail(PKV_EINVAL, "rtt_stride=%lld is smaller than max_kv_len=%d", (long long)rtt_stride, params->max_kv_len);
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.f)) return fail(PKV_EINVAL, "sm_scale must be finite and > 0");
-  const bool fp8 = params->kv_dtype == PKV_FP8_E4M3;
+  const bool fp8 = pkv::is_8bit(*params);
   if (!fp8) {
     if (sfq) return fail(PKV_EINVAL, "sfq is unsupported by a bf16 plan");
     if (sfk) return fail(PKV_EINVAL, "sfk is unsupported by a bf16 plan");
     if (sfv) return fail(PKV_EINVAL, "sfv is unsupported by a bf16 plan");
     if (v_mean) return fail(PKV_EINVAL, "v_mean is unsupported by a bf16 plan");
   } else if (batch > 0 && (!sfq || !sfk || !sfv)) {
-    return fail(PKV_EINVAL, "the fp8_e4m3 decode needs sfq, sfk and sfv");
+    return fail(PKV_EINVAL, "the 8-bit decode needs sfq, sfk and sfv");
   }
   if (batch == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !req_to_token || !seq_lens || !workspace)
@@ -324,7 +327,7 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
     return fail(PKV_EUNSUPPORTED, "decode grid of %lld work items x %lld kv-head units exceeds int32",
                 (long long)w.capacity, (long long)units);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fp8 ? pkv::launch_decode_fp8(a, params->head_dim, w.capacity, batch, s)
+  hipError_t e = fp8 ? pkv::launch_decode_fp8(a, params->kv_dtype == PKV_SAGE_INT8, w.capacity, batch, s)
                      : pkv::launch_decode_bf16(a, params->head_dim, w.capacity, batch, s);
   if (e != hipSuccess) return check_launch(e, "attn_decode launch");
   return check_launch(pkv::launch_decode_merge(a, params->head_dim, w.capacity, batch, s), "attn_decode merge launch");

@@ -72,7 +72,8 @@ inline int64_t decode_target_items(const pkv_params& p, int64_t resident_items) 
 // Granularity of the automatic decode chunks: the decode kernel's tile (32
 // tokens for bf16 K/V, 64 for 8-bit), so segment bounds inside a request fall
 // on tile bounds and no tile is cut short except at a request's end.
-inline int decode_plan_tile(const pkv_params& p) { return p.kv_dtype == PKV_FP8_E4M3 ? 64 : kDecodeTile; }
+inline bool is_8bit(const pkv_params& p) { return p.kv_dtype == PKV_FP8_E4M3 || p.kv_dtype == PKV_SAGE_INT8; }
+inline int decode_plan_tile(const pkv_params& p) { return is_8bit(p) ? 64 : kDecodeTile; }
 
 inline int64_t decode_capacity(const pkv_params& p, int64_t batch, int64_t target_items) {
   const int64_t tile = decode_plan_tile(p);
@@ -221,14 +222,14 @@ hipError_t launch_kv_store(void* k_pool, void* v_pool, int64_t pool_slots, const
                            int64_t row_bytes, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
                               hipStream_t s);
-hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
-                             hipStream_t s);
+// qk_int8: Q and K hold int8 codes (PKV_SAGE_INT8), else E4M3 bytes.
+hipError_t launch_decode_fp8(const DecodeArgs& a, bool qk_int8, int64_t capacity, int32_t batch, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
                                hipStream_t s);
 // Work items (all their waves) of a decode launch that the current device
 // holds at once, from the kernel's occupancy and the CU count.
 hipError_t decode_bf16_resident_items(int head_dim, int units, int64_t* items);
-hipError_t decode_fp8_resident_items(int units, int64_t* items);
+hipError_t decode_fp8_resident_items(int units, bool qk_int8, int64_t* items);
 hipError_t resident_items_of(const void* kernel, int wpb, int units, int64_t* items);
 // Waves per workgroup the decode launchers use for `units` waves per item.
 inline int decode_waves_per_block(int units) { return units >= 8 ? 8 : (units >= 4 ? 4 : (units >= 2 ? 2 : 1)); }

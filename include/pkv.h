@@ -80,7 +80,9 @@ typedef enum pkv_status {
 
 typedef enum pkv_dtype {
   PKV_BF16 = 0,
-  PKV_FP8_E4M3 = 1 /* OCP E4M3FN: 1-4-3, bias 7, largest finite 448 */
+  PKV_FP8_E4M3 = 1, /* OCP E4M3FN: 1-4-3, bias 7, largest finite 448 */
+  PKV_SAGE_INT8 = 2 /* Sage with INT8 Q and K (two's complement) and E4M3 V: the
+                       FlashInfer PrimTS Sage page, code §3 and §4.  DECODE only */
 } pkv_dtype;
 
 typedef enum pkv_mode { PKV_DECODE = 0, PKV_EXTEND = 1 } pkv_mode;
@@ -92,7 +94,8 @@ typedef struct pkv_params {
   int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0 */
   int32_t head_dim;     /* d: 64 or 128 */
   int32_t page_size;    /* power of two in [1, 256]; informational (reads are per token) */
-  int32_t kv_dtype;     /* pkv_dtype; PKV_FP8_E4M3 needs head_dim 128 (and q_block 1 for EXTEND) */
+  int32_t kv_dtype;     /* pkv_dtype; the 8-bit types need head_dim 128 (PKV_FP8_E4M3: q_block 1
+                           for EXTEND; PKV_SAGE_INT8: DECODE plans only) */
   int32_t q_block;      /* 8-bit: q rows per sfQ block (DECODE: one row per request; EXTEND: 1); else 0 */
   int32_t k_block;      /* 8-bit: key positions per sfK block, a multiple of 16; else 0 */
   int32_t max_kv_len;   /* upper bound of seq_lens (1 .. 2^30, <= rtt_stride of the run calls) */
@@ -169,7 +172,9 @@ int pkv_block_sparse_table(const pkv_params* params, int32_t batch, const int32_
 /* DECODE: one query row per request (q, out: [B, Hq, d]; [B*n, Hq, d] with
  * params->decode_q_len = n).  bf16 path: q and
  * pools bf16, sfq/sfk/sfv/v_mean must be NULL.  8-bit path (kv_dtype ==
- * PKV_FP8_E4M3): q and pools hold E4M3 bytes and the Sage formula applies:
+ * PKV_FP8_E4M3): q and pools hold E4M3 bytes; kv_dtype == PKV_SAGE_INT8: q
+ * and the K pool hold int8 codes (q8·k8 is the exact integer dot product)
+ * and the V pool E4M3 bytes.  Both apply the Sage formula:
  * S = sm_scale·sfq[b,h]·sfk[b,g,j/k_block]·(q8·k8), P stored as E4M3 of
  * 448·exp(S - m), O = sfv[b,g,:]·(Σ P8·v8)/(448·l) (+ v_mean[b,g,:]), where l
  * sums the unquantised exp(S - m).  sfq float [B*decode_q_len, Hq], sfk float

@@ -29,6 +29,25 @@ def dev_u8(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to("cuda")
 
 
+def dev_i8(x):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int8)).to("cuda")
+
+
+def dev_qk8(x, spec):
+    """Q or K codes of an 8-bit batch: int8 for the INT8 Sage dtype, else E4M3 bytes."""
+    return dev_i8(x) if spec.dtype == "int8" else dev_u8(x)
+
+
+def kv_dtype_of(pkv, spec):
+    return pkv.PKV_SAGE_INT8 if spec.dtype == "int8" else pkv.PKV_FP8_E4M3
+
+
+def qk_codes_of(spec):
+    """How the oracle reads the batch's Q and K bytes."""
+    return "int8" if spec.dtype == "int8" else "e4m3"
+
+
 def dev_f32(x):
     torch = torch_mod()
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda")

@@ -50,6 +50,8 @@ def _ws(lib, params, mode=pkv.PKV_DECODE, batch=4, total_q=0):
     (dict(kv_dtype=7), pkv.PKV_EUNSUPPORTED, "kv_dtype=7"),
     (dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=20, q_block=1), pkv.PKV_EINVAL, "k_block=20"),
     (dict(kv_dtype=pkv.PKV_FP8_E4M3, k_block=64, q_block=1, head_dim=64), pkv.PKV_EUNSUPPORTED, "head_dim=128"),
+    (dict(kv_dtype=pkv.PKV_SAGE_INT8, k_block=64, q_block=1, head_dim=64), pkv.PKV_EUNSUPPORTED, "head_dim=128"),
+    (dict(kv_dtype=pkv.PKV_SAGE_INT8, k_block=24, q_block=1), pkv.PKV_EINVAL, "k_block=24"),
     (dict(decode_q_len=-1), pkv.PKV_EINVAL, "decode_q_len=-1"),
     (dict(decode_q_len=65), pkv.PKV_EINVAL, "decode_q_len=65"),
 ])
@@ -85,6 +87,24 @@ def test_fp8_extend_plans_take_one_sfq_per_row(lib):
     assert rc == pkv.PKV_EUNSUPPORTED and "q_block=1" in pkv.last_error()
     rc, ws, sc = _ws(lib, p, mode=pkv.PKV_DECODE)
     assert rc == pkv.PKV_OK and ws > 0 and sc > 0
+
+
+def test_int8_sage_is_a_decode_path(lib):
+    """INT8 Q/K (the Sage page's code §3) is planned for DECODE; an EXTEND plan
+    is rejected, as is an int8 extend call."""
+    p = pkv.Params(32, 8, 128, 16, 4096, kv_dtype=pkv.PKV_SAGE_INT8, q_block=1, k_block=64)
+    rc, ws, sc = _ws(lib, p, mode=pkv.PKV_DECODE)
+    assert rc == pkv.PKV_OK and ws > 0 and sc > 0
+    rc, _, _ = _ws(lib, p, mode=pkv.PKV_EXTEND, total_q=100)
+    assert rc == pkv.PKV_EUNSUPPORTED and "sage_int8 is a DECODE path" in pkv.last_error()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    rc = lib.pkv_attn_extend(ctypes.byref(p), fake, None, fake, fake, fake, 100, fake, 4096, None, fake, fake, 4,
+                             16, 0.1, fake, fake, fake, None, fake, 1 << 20, None, 0, None)
+    assert rc == pkv.PKV_EUNSUPPORTED and "DECODE path" in pkv.last_error()
+    # the decode needs its scales, like the E4M3 one
+    rc = lib.pkv_attn_decode(ctypes.byref(p), fake, None, fake, fake, fake, 100, fake, 4096, None, fake, 4,
+                             0.1, None, fake, fake, None, fake, 1 << 20, fake, 1 << 20, None)
+    assert rc == pkv.PKV_EINVAL and "needs sfq, sfk and sfv" in pkv.last_error()
 
 
 def test_run_call_argument_errors(lib):

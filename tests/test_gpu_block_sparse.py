@@ -5,8 +5,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import (FP8_REL_L2, assert_bf16_close, assert_lse_close, dev_bf16, dev_f32, dev_i32, dev_u8, host,
-                      rel_l2, torch_mod)
+from gpu_util import (FP8_REL_L2, assert_bf16_close, assert_lse_close, dev_bf16, dev_f32, dev_i32, dev_qk8, dev_u8,
+                      host, kv_dtype_of, qk_codes_of, rel_l2, torch_mod)
 from workloads import SPECS, Spec, block_mask, make_device_batch, make_host_batch, pool_before_store, round_bf16
 
 pytestmark = pytest.mark.gpu
@@ -45,13 +45,13 @@ def run_sparse(hb, indptr, idx, bs, v_mean=None, sm_scale=None, rpi=None, rtt_ro
     pkv = _pkv()
     lay = hb.layout
     spec = lay.spec
-    fp8 = spec.dtype == "fp8"
+    fp8 = spec.dtype in ("fp8", "int8")
     rtt_host = lay.req_to_token if rtt_rows is None else rtt_rows
     if fp8:
-        kw = dict(kv_dtype=pkv.PKV_FP8_E4M3, q_block=spec.q_block, k_block=spec.k_block)
-        k_pool = dev_u8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F))
+        kw = dict(kv_dtype=kv_dtype_of(pkv, spec), q_block=spec.q_block, k_block=spec.k_block)
+        k_pool = dev_qk8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F), spec)
         v_pool = dev_u8(pool_before_store(hb.v_codes, lay.new_slots, fill=0x7F))
-        k_new, v_new, q = dev_u8(hb.k_new_codes), dev_u8(hb.v_new_codes), dev_u8(hb.q_codes)
+        k_new, v_new, q = dev_qk8(hb.k_new_codes, spec), dev_u8(hb.v_new_codes), dev_qk8(hb.q_codes, spec)
         sfk = dev_f32(hb.sfk)
     else:
         kw = {}
@@ -77,10 +77,10 @@ def run_sparse(hb, indptr, idx, bs, v_mean=None, sm_scale=None, rpi=None, rtt_ro
 
 def oracle_sparse(hb, indptr, idx, bs, v_mean=None, sm_scale=None):
     lay = hb.layout
-    if lay.spec.dtype == "fp8":
+    if lay.spec.dtype in ("fp8", "int8"):
         return oracle.block_sparse_sage_decode(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens,
                                                indptr, idx, bs, hb.sfq, hb.sfk, hb.sfv, lay.spec.k_block,
-                                               sm_scale=sm_scale, v_mean=v_mean)
+                                               sm_scale=sm_scale, v_mean=v_mean, qk_codes=qk_codes_of(lay.spec))
     return oracle.block_sparse_decode(round_bf16(hb.q), round_bf16(hb.k_pool), round_bf16(hb.v_pool),
                                       lay.req_to_token, lay.seq_lens, indptr, idx, bs, sm_scale=sm_scale)
 
@@ -145,6 +145,22 @@ def test_req_pool_indices_rows():
     ro, rlse = oracle_sparse(hb, indptr, idx, bs)
     assert_bf16_close(o, ro, "block-sparse rpi")
     assert_lse_close(lse, rlse)
+
+
+@pytest.mark.parametrize("bs,density", [(64, 0.1), (128, 0.3), (256, 0.5)])
+def test_int8_matches_block_sparse_sage_oracle(bs, density):
+    """INT8 Q/K codes (the Sage page's code §3) on the compacted table."""
+    spec = Spec("bs_i8", "decode", 6, 32, 8, 128, 16, (0, 2000), 1, dtype="int8", k_block=64)
+    hb = make_host_batch(spec, 12)
+    indptr, idx = mask_with_edges(hb.layout, bs, density, 13, empty=(4,), junk=True)
+    vm = np.random.default_rng(14).standard_normal((spec.batch, spec.num_kv_heads, 128)).astype(np.float32)
+    o, lse, _ = run_sparse(hb, indptr, idx, bs, v_mean=vm)
+    ro, rlse = oracle_sparse(hb, indptr, idx, bs, v_mean=vm)
+    assert np.all(np.isfinite(o))
+    assert rel_l2(o, ro) <= FP8_REL_L2
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.abs(lse[fin] - rlse[fin]).max() <= 1e-3
 
 
 @pytest.mark.parametrize("bs,density", [(64, 0.1), (128, 0.3), (256, 0.5)])

@@ -4,7 +4,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import FP8_REL_L2, dev_f32, dev_i32, dev_u8, host, rel_l2, torch_mod
+from gpu_util import (FP8_REL_L2, dev_f32, dev_i32, dev_qk8, dev_u8, host, kv_dtype_of, qk_codes_of, rel_l2,
+                      torch_mod)
 from workloads import SPECS, Spec, make_device_batch, make_host_batch, pool_before_store
 
 pytestmark = pytest.mark.gpu
@@ -20,18 +21,20 @@ def run_fp8(hb, kv_chunk=0, v_mean=None, sm_scale=None, split_target=0, seq_lens
     pkv = _pkv()
     lay = hb.layout
     spec = lay.spec
-    k_pool = dev_u8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F))
+    k_pool = dev_qk8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F), spec)
     v_pool = dev_u8(pool_before_store(hb.v_codes, lay.new_slots, fill=0x7F))
     params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
-                        max_kv_len=lay.req_to_token.shape[1], kv_dtype=pkv.PKV_FP8_E4M3,
+                        max_kv_len=lay.req_to_token.shape[1], kv_dtype=kv_dtype_of(pkv, spec),
                         q_block=spec.q_block, k_block=spec.k_block, kv_chunk=kv_chunk,
                         split_target=split_target)
     seq = dev_i32(lay.seq_lens if seq_lens is None else seq_lens)
     rtt = dev_i32(lay.req_to_token)
     plan = pkv.plan_metadata(params, pkv.PKV_DECODE, seq)
-    pkv.kv_store(params, k_pool, v_pool, dev_u8(hb.k_new_codes), dev_u8(hb.v_new_codes), dev_i32(lay.new_slots))
+    pkv.kv_store(params, k_pool, v_pool, dev_qk8(hb.k_new_codes, spec), dev_u8(hb.v_new_codes),
+                 dev_i32(lay.new_slots))
     lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
-    out = pkv.attn_decode(params, dev_u8(hb.q_codes), k_pool, v_pool, rtt, seq, plan, lse=lse, sm_scale=sm_scale,
+    out = pkv.attn_decode(params, dev_qk8(hb.q_codes, spec), k_pool, v_pool, rtt, seq, plan, lse=lse,
+                          sm_scale=sm_scale,
                           sfq=dev_f32(hb.sfq), sfk=dev_f32(hb.sfk), sfv=dev_f32(hb.sfv),
                           v_mean=None if v_mean is None else dev_f32(v_mean))
     torch.cuda.synchronize()
@@ -42,7 +45,8 @@ def oracle_fp8(hb, v_mean=None, sm_scale=None, seq_lens=None):
     lay = hb.layout
     seq = lay.seq_lens if seq_lens is None else seq_lens
     return oracle.sage_decode(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, seq, hb.sfq, hb.sfk,
-                              hb.sfv, lay.spec.k_block, sm_scale=sm_scale, v_mean=v_mean)
+                              hb.sfv, lay.spec.k_block, sm_scale=sm_scale, v_mean=v_mean,
+                              qk_codes=qk_codes_of(lay.spec))
 
 
 SMALL = Spec("f8_small", "decode", 6, 32, 8, 128, 16, (0, 700), 1, dtype="fp8", k_block=64)
@@ -59,6 +63,55 @@ def test_fp8_decode_matches_sage_oracle(seed, k_block):
     rel = rel_l2(o, ro)
     assert rel <= FP8_REL_L2, rel
     assert np.abs(lse - rlse).max() <= 1e-3
+
+
+SMALL_I8 = Spec("i8_small", "decode", 6, 32, 8, 128, 16, (0, 700), 1, dtype="int8", k_block=64)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("k_block", [64, 16])
+def test_int8_decode_matches_sage_oracle(seed, k_block):
+    """INT8 Q and K codes (the Sage page's code §3 and §4), E4M3 V."""
+    from dataclasses import replace
+    hb = make_host_batch(replace(SMALL_I8, k_block=k_block), 40 + seed)
+    o, lse = run_fp8(hb)
+    ro, rlse = oracle_fp8(hb)
+    assert np.all(np.isfinite(o))
+    assert rel_l2(o, ro) <= FP8_REL_L2, rel_l2(o, ro)
+    assert np.abs(lse - rlse).max() <= 1e-3
+
+
+def test_int8_extreme_codes_and_split_merge_with_v_mean():
+    """Codes at -128 and 127 in Q and K (int32 dot products up to 2^21) through
+    split chunks and the merge, against the oracle."""
+    hb = make_host_batch(SMALL_I8, 45)
+    rng = np.random.default_rng(46)
+    hb.q_codes = rng.choice(np.array([-128, -127, 0, 127], np.int8), size=hb.q_codes.shape)
+    ext = rng.random(hb.k_codes.shape) < 0.5
+    hb.k_codes = np.where(ext, rng.choice(np.array([-128, 127], np.int8), size=hb.k_codes.shape), hb.k_codes)
+    hb.k_new_codes = hb.k_codes[hb.layout.new_slots].copy()
+    # keep the scores in a range where softmax is not a one-hot: scale the Q/K steps down
+    hb.sfq = (hb.sfq / 64).astype(np.float32)
+    vm = rng.uniform(-1, 1, size=hb.sfv.shape).astype(np.float32)
+    o1, l1 = run_fp8(hb, kv_chunk=64, v_mean=vm)
+    o2, l2 = run_fp8(hb, v_mean=vm)
+    ro, rlse = oracle_fp8(hb, v_mean=vm)
+    assert rel_l2(o1, ro) <= FP8_REL_L2 and rel_l2(o2, ro) <= FP8_REL_L2
+    assert np.abs(l1 - rlse).max() <= 1e-3 and np.abs(l2 - rlse).max() <= 1e-3
+
+
+@pytest.mark.parametrize("n,hq,hkv,kv_chunk,with_vm", [(2, 32, 8, 0, False), (4, 32, 8, 64, True), (3, 16, 2, 0, True)])
+def test_int8_several_new_tokens_per_request(n, hq, hkv, kv_chunk, with_vm):
+    spec = Spec("i8_multi", "decode", 5, hq, hkv, 128, 16, (0, 900), n, dtype="int8", k_block=64)
+    hb = make_host_batch(spec, 50 + n)
+    lay = hb.layout
+    vm = np.random.default_rng(150 + n).standard_normal((spec.batch, hkv, 128)).astype(np.float32) if with_vm else None
+    o, l, sfq_rows = run_fp8_multi(hb, n, v_mean=vm, kv_chunk=kv_chunk)
+    ro, rl = oracle.sage_extend(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens,
+                                lay.cu_seqlens_q, sfq_rows, hb.sfk, hb.sfv, spec.k_block, v_mean=vm, qk_codes="int8")
+    assert np.all(np.isfinite(o))
+    assert rel_l2(o, ro) <= FP8_REL_L2, rel_l2(o, ro)
+    assert np.abs(l - rl).max() <= 1e-3
 
 
 def test_fp8_split_merge_and_v_mean():
@@ -146,16 +199,18 @@ def run_fp8_multi(hb, n, v_mean=None, kv_chunk=0, seed=None):
     B, hq, hkv = spec.batch, spec.num_q_heads, spec.num_kv_heads
     rng = np.random.default_rng(n if seed is None else seed)
     sfq_rows = (hb.sfq[np.repeat(np.arange(B), n)] * rng.uniform(0.8, 1.25, (B * n, hq))).astype(np.float32)
-    k_pool = dev_u8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F))
+    k_pool = dev_qk8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F), spec)
     v_pool = dev_u8(pool_before_store(hb.v_codes, lay.new_slots, fill=0x7F))
     params = pkv.Params(hq, hkv, 128, spec.page_size, max_kv_len=lay.req_to_token.shape[1],
-                        kv_dtype=pkv.PKV_FP8_E4M3, q_block=1, k_block=spec.k_block, kv_chunk=kv_chunk,
+                        kv_dtype=kv_dtype_of(pkv, spec), q_block=1, k_block=spec.k_block, kv_chunk=kv_chunk,
                         decode_q_len=n)
     seq = dev_i32(lay.seq_lens)
     plan = pkv.plan_metadata(params, pkv.PKV_DECODE, seq)
-    pkv.kv_store(params, k_pool, v_pool, dev_u8(hb.k_new_codes), dev_u8(hb.v_new_codes), dev_i32(lay.new_slots))
+    pkv.kv_store(params, k_pool, v_pool, dev_qk8(hb.k_new_codes, spec), dev_u8(hb.v_new_codes),
+                 dev_i32(lay.new_slots))
     lse = torch.empty((B * n, hq), dtype=torch.float32, device="cuda")
-    out = pkv.attn_decode(params, dev_u8(hb.q_codes), k_pool, v_pool, dev_i32(lay.req_to_token), seq, plan, lse=lse,
+    out = pkv.attn_decode(params, dev_qk8(hb.q_codes, spec), k_pool, v_pool, dev_i32(lay.req_to_token), seq, plan,
+                          lse=lse,
                           sfq=dev_f32(sfq_rows), sfk=dev_f32(hb.sfk), sfv=dev_f32(hb.sfv),
                           v_mean=None if v_mean is None else dev_f32(v_mean))
     torch.cuda.synchronize()

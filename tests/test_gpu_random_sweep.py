@@ -132,3 +132,40 @@ def test_random_block_sparse_decode():
         else:
             assert_bf16_close(o, ro, what)
             assert_lse_close(lse, rlse, what)
+
+
+def test_random_int8_decode():
+    """INT8 Q/K Sage decode: one and several new tokens, dense and block-sparse."""
+    from test_gpu_block_sparse import mask_with_edges, oracle_sparse, run_sparse
+    from test_gpu_decode_fp8 import oracle_fp8, run_fp8, run_fp8_multi
+    rng = np.random.default_rng(2028)
+    for case in range(CASES // 2):
+        B, hq, hkv, d, page = _draw_shape(rng, d_choices=(128,))
+        k_block = int(rng.choice([16, 32, 64]))
+        kind = ("one", "multi", "sparse")[case % 3]
+        n = int(rng.choice([2, 3, 4])) if kind == "multi" else 1
+        spec = Spec(f"ri8{case}", "decode", B, hq, hkv, d, page, _lengths(rng, B, 0, 900), n, dtype="int8",
+                    k_block=64 if kind == "sparse" else k_block)
+        hb = make_host_batch(spec, 300 + case)
+        vm = rng.standard_normal((B, hkv, d)).astype(np.float32) if case % 2 == 0 else None
+        what = f"case {case}: {kind} B={B} hq={hq} hkv={hkv} page={page} n={n} k_block={spec.k_block}"
+        if kind == "one":
+            o, lse = run_fp8(hb, v_mean=vm)
+            ro, rlse = oracle_fp8(hb, v_mean=vm)
+        elif kind == "multi":
+            lay = hb.layout
+            o, lse, sfq_rows = run_fp8_multi(hb, n, v_mean=vm)
+            ro, rlse = oracle.sage_extend(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens,
+                                          lay.cu_seqlens_q, sfq_rows, hb.sfk, hb.sfv, spec.k_block, v_mean=vm,
+                                          qk_codes="int8")
+        else:
+            bs = int(rng.choice([64, 128]))
+            indptr, idx = mask_with_edges(hb.layout, bs, float(rng.choice([0.1, 0.5])), case)
+            o, lse, _ = run_sparse(hb, indptr, idx, bs, v_mean=vm)
+            ro, rlse = oracle_sparse(hb, indptr, idx, bs, v_mean=vm)
+        assert np.all(np.isfinite(o)), what
+        assert rel_l2(o, ro) <= FP8_REL_L2, (what, rel_l2(o, ro))
+        fin = np.isfinite(rlse)
+        assert np.array_equal(np.isfinite(lse), fin), what
+        if fin.any():
+            assert np.abs(lse[fin] - rlse[fin]).max() <= 1e-3, what
