@@ -52,6 +52,7 @@ KERNEL_SOURCES = {
     "long_decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "single_decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "decode_fp8": ["decode_fp8.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
+    "decode_int8": ["decode_fp8.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h"],
     "extend_bf16": ["extend_bf16.hip", "lds_dma.h", "plan.hip", "device_common.h"],
     "extend_fp8": ["extend_fp8.hip", "lds_dma.h", "plan.hip", "device_common.h"],
     "sparse_decode_bf16": ["decode_bf16.hip", "decode_stream.h", "decode_merge.h", "plan.hip", "device_common.h",
@@ -88,6 +89,7 @@ CALL_KERNELS = {
     "long_decode_bf16": ("decode_bf16_kernel", "decode_merge"),
     "single_decode_bf16": ("decode_bf16_kernel", "decode_merge"),
     "decode_fp8": ("decode_fp8_kernel", "decode_merge"),
+    "decode_int8": ("decode_fp8_kernel", "decode_merge"),
     "decode_n4_bf16": ("decode_bf16_kernel", "decode_merge"),
     "extend_bf16": ("extend_bf16_kernel",),
     "extend_fp8": ("extend_fp8_kernel",),
@@ -162,16 +164,21 @@ def copy_calibration():
 
 
 # ---------------------------------------------------------------- workloads
+KV_DTYPE_NAMES = {"bf16": "bf16", "fp8": "fp8_e4m3", "int8": "int8 q/k (sage), fp8_e4m3 v"}
+
+
 class DecodeRunner:
     def __init__(self, name, layers, torch, pkv, workloads):
         self.torch, self.pkv = torch, pkv
         spec = workloads.SPECS[name]
         self.spec = spec
-        self.fp8 = spec.dtype == "fp8"
+        self.fp8 = spec.dtype in ("fp8", "int8")  # the 8-bit Sage path (E4M3, or INT8 Q/K)
+        self.qk_codes = "int8" if spec.dtype == "int8" else "e4m3"
         self.db = workloads.make_device_batch(spec, seed=0, layers=layers)
         lay = self.db.layout
         self.layers = layers
-        kw = dict(kv_dtype=pkv.PKV_FP8_E4M3, q_block=spec.q_block, k_block=spec.k_block) if self.fp8 else {}
+        kv_dtype = pkv.PKV_SAGE_INT8 if spec.dtype == "int8" else pkv.PKV_FP8_E4M3
+        kw = dict(kv_dtype=kv_dtype, q_block=spec.q_block, k_block=spec.k_block) if self.fp8 else {}
         self.q_len = int(lay.new_lens[0])  # new tokens per request
         self.params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
                                  max_kv_len=lay.req_to_token.shape[1], decode_q_len=self.q_len, **kw)
@@ -213,7 +220,7 @@ class DecodeRunner:
         return {"workload": s.name, "batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
                 "head_dim": s.head_dim, "page_size": s.page_size,
                 "cached_len": f"{cached} + {self.q_len} new token{'s' if self.q_len > 1 else ''}",
-                "kv_dtype": "fp8_e4m3" if self.fp8 else "bf16", "layers_per_step": self.layers,
+                "kv_dtype": KV_DTYPE_NAMES[s.dtype], "layers_per_step": self.layers,
                 "kv_bytes_per_layer": self.kv_bytes_per_layer}
 
     def roofline(self, avg_launch_s, workload):
@@ -246,7 +253,7 @@ class DecodeRunner:
             L = lay.seq_lens[b:b + 1]
             if self.fp8:
                 oracle.sage_decode(q[b:b + 1], kp, vp, rtt, L, sfq[b:b + 1], sfk[b:b + 1], sfv[b:b + 1],
-                                   k_block=spec.k_block)
+                                   k_block=spec.k_block, qk_codes=self.qk_codes)
             else:
                 nq = self.q_len
                 oracle.paged_attention(q[b * nq:(b + 1) * nq], kp, vp, rtt, L, [0, nq])
@@ -320,7 +327,7 @@ class SparseDecodeRunner(DecodeRunner):
             rtt, L = lay.req_to_token[b:b + 1], lay.seq_lens[b:b + 1]
             if self.fp8:
                 oracle.block_sparse_sage_decode(q[b:b + 1], kp, vp, rtt, L, ip, blocks, bs, sfq[b:b + 1],
-                                                sfk[b:b + 1], sfv[b:b + 1], spec.k_block)
+                                                sfk[b:b + 1], sfv[b:b + 1], spec.k_block, qk_codes=self.qk_codes)
             else:
                 oracle.block_sparse_decode(q[b:b + 1], kp, vp, rtt, L, ip, blocks, bs)
             sel = sum(max(0, min(bs, int(L[0]) - int(k) * bs)) for k in blocks)
@@ -391,12 +398,14 @@ class ExtendRunner:
                 "algorithmic_flops_per_launch": self.flops_per_layer, "avg_launch_us": round(avg_launch_s * 1e6, 2)}
 
 
-RUNNERS = {"decode_bf16": DecodeRunner, "long_decode_bf16": DecodeRunner, "single_decode_bf16": DecodeRunner, "decode_fp8": DecodeRunner,
+RUNNERS = {"decode_bf16": DecodeRunner, "long_decode_bf16": DecodeRunner, "single_decode_bf16": DecodeRunner,
+           "decode_fp8": DecodeRunner, "decode_int8": DecodeRunner,
            "decode_n4_bf16": DecodeRunner, "extend_bf16": ExtendRunner, "extend_fp8": ExtendRunner,
            "sparse_decode_bf16": SparseDecodeRunner, "sparse_decode_fp8": SparseDecodeRunner}
-UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "single_decode_bf16": "GB/s", "decode_fp8": "GB/s", "decode_n4_bf16": "GB/s",
+UNITS = {"decode_bf16": "GB/s", "long_decode_bf16": "GB/s", "single_decode_bf16": "GB/s", "decode_fp8": "GB/s",
+         "decode_int8": "GB/s", "decode_n4_bf16": "GB/s",
          "extend_bf16": "TFLOP/s", "extend_fp8": "TFLOP/s", "sparse_decode_bf16": "GB/s", "sparse_decode_fp8": "GB/s"}
-DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "single_decode_bf16": 4, "decode_fp8": 4, "decode_n4_bf16": 4, "extend_bf16": 4,
+DEFAULT_LAYERS = {"decode_bf16": 4, "long_decode_bf16": 2, "single_decode_bf16": 4, "decode_fp8": 4, "decode_int8": 4, "decode_n4_bf16": 4, "extend_bf16": 4,
                   "extend_fp8": 4, "sparse_decode_bf16": 2, "sparse_decode_fp8": 2}
 
 
@@ -461,7 +470,7 @@ def main():
     ap.add_argument("--workload", default="decode_bf16", choices=sorted(RUNNERS))
     ap.add_argument("--layers", type=int, default=0, help="layers (distinct K/V pools) per step")
     ap.add_argument("--secondary", default="extend_bf16,long_decode_bf16,decode_fp8,decode_n4_bf16,extend_fp8,"
-                                           "sparse_decode_bf16,sparse_decode_fp8,single_decode_bf16",
+                                           "sparse_decode_bf16,sparse_decode_fp8,single_decode_bf16,decode_int8",
                     help="comma list of workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -499,7 +508,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": UNITS[args.workload], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3" if getattr(runner, "fp8", False) else "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3", "int8": "int8/fp8_e4m3"}.get(runner.spec.dtype, "bf16"),
         "data": "synthetic", "config": runner.describe(),
         "launch": ("hip_graph" if graph else "eager") + (", plan per layer" if args.plan_per_layer else ""),
         "roofline": roof,

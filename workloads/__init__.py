@@ -25,6 +25,9 @@ name                   description
 ``decode_fp8``         B=64, 32/8 heads, d=128, page 16, cached U[1024,8192];
                        E4M3 codes of N(0,1)/scale with per-64-token sfK,
                        per-(b,h) sfQ and per-channel sfV drawn from U[0.5,2]
+``decode_int8``        as ``decode_fp8`` with INT8 Q and K codes (Sage INT8:
+                       clip(rint(N(0,1)/sf), -127, 127), sf = U[0.5,2]/16)
+                       and E4M3 V
 ``decode_n4_bf16``     as ``decode_bf16`` with 4 new tokens per request
                        checked in one decode call (a verify step)
 ``extend_fp8``         as ``extend_bf16`` with E4M3 K/V, sfQ per new-token
@@ -91,6 +94,8 @@ SPECS = {
                        k_block=16, q_block=1),
     "decode_fp8": Spec("decode_fp8", "decode", 64, 32, 8, 128, 16, (1024, 8192), 1,
                        dtype="fp8", k_block=64, q_block=1),
+    "decode_int8": Spec("decode_int8", "decode", 64, 32, 8, 128, 16, (1024, 8192), 1,
+                        dtype="int8", k_block=64, q_block=1),
     "sparse_decode_bf16": Spec("sparse_decode_bf16", "decode", 8, 40, 40, 128, 16, (15360, 75600), 1,
                                sparse_block=64, density=0.10),
     "sparse_decode_fp8": Spec("sparse_decode_fp8", "decode", 8, 40, 40, 128, 16, (15360, 75600), 1,
@@ -100,7 +105,7 @@ SPECS = {
 # Index used to derive the seed of each named workload (1000 + index).
 SPEC_INDEX = {"tiny_decode": 1, "tiny_extend": 1, "decode_bf16": 2, "extend_bf16": 3, "decode_n4_bf16": 6, "extend_fp8": 7,
               "long_decode_bf16": 4, "decode_fp8": 5, "sparse_decode_bf16": 8, "sparse_decode_fp8": 10,
-              "single_decode_bf16": 11}
+              "single_decode_bf16": 11, "decode_int8": 12}
 
 
 def seed_sequence(spec: Spec, seed: int) -> list:
