@@ -157,14 +157,17 @@ def test_fp8_constant_scores_closed_form():
     assert rel_l2(o, ro) <= 4e-3  # only bf16 output rounding and fp32 sums remain
 
 
-def test_full_size_fp8_decode_sampled():
+@pytest.mark.parametrize("name", ["decode_fp8", "decode_int8"])
+def test_full_size_8bit_decode_sampled(name):
+    """The full 8-bit decode workloads (E4M3, and INT8 Q/K) in the bench's
+    launch configuration, 24 sampled requests recomputed by the oracle."""
     torch = torch_mod()
     pkv = _pkv()
-    spec = SPECS["decode_fp8"]
+    spec = SPECS[name]
     db = make_device_batch(spec, seed=0, layers=1)
     lay = db.layout
     params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
-                        max_kv_len=lay.req_to_token.shape[1], kv_dtype=pkv.PKV_FP8_E4M3,
+                        max_kv_len=lay.req_to_token.shape[1], kv_dtype=kv_dtype_of(pkv, spec),
                         q_block=spec.q_block, k_block=spec.k_block)
     plan = pkv.plan_metadata(params, pkv.PKV_DECODE, db.seq_lens)
     pkv.kv_store(params, db.k_pools[0], db.v_pools[0], db.k_new[0], db.v_new[0], db.new_slots)
@@ -182,7 +185,8 @@ def test_full_size_fp8_decode_sampled():
         k8 = db.k_pools[0][rows].cpu().numpy()
         v8 = db.v_pools[0][rows].cpu().numpy()
         o, _ = oracle.sage_decode(q8, k8, v8, np.arange(L)[None], [L], db.sfq[b:b + 1].cpu().numpy(),
-                                  db.sfk[b:b + 1].cpu().numpy(), db.sfv[b:b + 1].cpu().numpy(), spec.k_block)
+                                  db.sfk[b:b + 1].cpu().numpy(), db.sfv[b:b + 1].cpu().numpy(), spec.k_block,
+                                  qk_codes=qk_codes_of(spec))
         got.append(host(out[b:b + 1]))
         ref.append(o)
         assert rel_l2(got[-1], o) <= FP8_REL_L2, b
