@@ -38,7 +38,8 @@
  *              request b is req_to_token[row(b) * rtt_stride + j], with
  *              row(b) = req_pool_indices[b] (or b when that pointer is NULL).
  *   pools      K and V pools of ONE layer, [pool_slots, Hkv, d] row-major,
- *              bf16 (or E4M3 bytes for the 8-bit decode).
+ *              bf16 (or E4M3 bytes on the 8-bit paths; int8 K and E4M3 V
+ *              with PKV_SAGE_INT8).
  *   q / out    [T, Hq, d] row-major (T = B in DECODE); out is bf16; lse is
  *              float [T, Hq], natural-log log-sum-exp of the scaled scores
  *              (-inf for a row with no keys), optional (NULL).
@@ -134,7 +135,9 @@ int pkv_plan_metadata(const pkv_params* params, int32_t mode, int32_t batch, int
 /* Store this step's new K/V rows (KV-cache paragraph of the SGLang pages:
  * the cache is updated inside the forward pass):
  * k_pool[slots[t]] = k_new[t] and v_pool[slots[t]] = v_new[t] for
- * t < num_tokens, each row [Hkv, d] of the params' kv_dtype.  k_new/v_new
+ * t < num_tokens, each row [Hkv, d] of the params' kv_dtype (bf16; one
+ * byte per element on the 8-bit paths: E4M3, or int8 K and E4M3 V for
+ * PKV_SAGE_INT8; rows are copied as bytes).  k_new/v_new
  * are [num_tokens, Hkv, d] device buffers; slots int32 [num_tokens] device,
  * distinct.  A slot outside [0, pool_slots) is skipped. */
 int pkv_kv_store(const pkv_params* params, void* k_pool, void* v_pool, int64_t pool_slots,
