@@ -7,7 +7,7 @@ for bit.  The SGLang basics page names graph capture of the decode forward
 import numpy as np
 import pytest
 
-from gpu_util import FP8_REL_L2, assert_bf16_close, host, rel_l2, torch_mod
+from gpu_util import FP8_REL_L2, assert_bf16_close, host, kv_dtype_of, qk_codes_of, rel_l2, torch_mod
 from workloads import Spec, make_device_batch
 
 import oracle
@@ -101,18 +101,20 @@ def _capture(step, torch):
     return graph, captured
 
 
-def test_block_sparse_step_graph_replays_equal_eager_runs():
+@pytest.mark.parametrize("dtype", ["fp8", "int8"])
+def test_block_sparse_step_graph_replays_equal_eager_runs(dtype):
     """The compacted table, the plan over its lengths and an 8-bit decode
-    captured once; replays with new block lists in the same buffers."""
+    (E4M3, or INT8 Q/K) captured once; replays with new block lists in the
+    same buffers."""
     from workloads import block_mask
     torch = torch_mod()
     pkv = _pkv()
-    spec = Spec("graph_sparse", "decode", 6, 16, 4, 128, 16, (300, 4000), 1, dtype="fp8", k_block=64)
+    spec = Spec("graph_sparse", "decode", 6, 16, 4, 128, 16, (300, 4000), 1, dtype=dtype, k_block=64)
     db = make_device_batch(spec, seed=4, layers=1)
     lay = db.layout
     B, Hq, d, bs = spec.batch, spec.num_q_heads, spec.head_dim, 128
     params = pkv.Params(Hq, spec.num_kv_heads, d, spec.page_size, max_kv_len=lay.req_to_token.shape[1],
-                        kv_dtype=pkv.PKV_FP8_E4M3, q_block=1, k_block=spec.k_block)
+                        kv_dtype=kv_dtype_of(pkv, spec), q_block=1, k_block=spec.k_block)
     ws_bytes, sc_bytes = pkv.workspace_size(params, pkv.PKV_DECODE, B)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     scratch = torch.empty(max(sc_bytes, 16), dtype=torch.uint8, device="cuda")
@@ -152,7 +154,7 @@ def test_block_sparse_step_graph_replays_equal_eager_runs():
         torch.cuda.synchronize()
         assert torch.equal(_bits(got_o), _bits(out)) and torch.equal(_bits(got_l), _bits(lse)), rep
         ro, _ = oracle.block_sparse_sage_decode(q8, k8, v8, lay.req_to_token, lay.seq_lens, ip, ix, bs, sfq, sfk,
-                                                sfv, spec.k_block)
+                                                sfv, spec.k_block, qk_codes=qk_codes_of(spec))
         assert rel_l2(host(got_o), ro) <= FP8_REL_L2, rep
 
 
