@@ -1,11 +1,14 @@
 """8-bit scaled ("Sage") decode attention in float64 (oracle; test infrastructure).
 
-Formula followed ([FlashInfer-Sage], code §1, the README "Sage attention"
-block), for one attention row r and key position c:
-
-    S[r][c] = sfQ[blkQ(r)] · sfK[blkK(c)] · (Q8 · K8ᵀ)[r][c]
-    P       = row softmax of S, stored as the E4M3 value of 448·p
-    O[r][d] = sfV[d] · (Σ_c P8[r][c] · V8[c][d]) / (448 · l[r])   (+ v_mean[d])
+What is computed ([FlashInfer-Sage], code §1 and the README "Sage attention"
+block), for one query row and the keys it sees: each score is the dot product
+of the row's Q codes with a key's K codes, multiplied by the Q scale of the
+row's block and by the K scale of the key's block.  The probabilities
+exp(score - row max) are kept as E4M3 codes of 448 times their value; the
+output channel d is the sum over keys of those codes times the key's V code
+in channel d, divided by 448 times the row sum l of the unquantised
+probabilities, times the channel's V scale (plus an optional per-channel
+mean of V).
 
 Scale conventions ([FlashInfer-Sage], code §1 and §4): the caller quantises
 and supplies the scales; Q and K scales enter before the row max and the

@@ -205,3 +205,51 @@ def test_reuse_of_slots_across_requests_is_allowed():
         torch.from_numpy(v[0].astype(np.float64)).permute(1, 0, 2).repeat_interleave(2, 0).contiguous(),
         scale=1 / math.sqrt(8))
     np.testing.assert_allclose(o[1], ref.permute(1, 0, 2).numpy()[0], rtol=1e-12, atol=1e-12)
+
+
+def _brute_force_row(q, keys, vals, sm_scale):
+    """Attention of one query over a list of keys, by explicit loops over plain
+    floats ([FA-vs-PA], FlashAttention §1: softmax of the scaled dot products,
+    then the weighted sum of the value rows)."""
+    scores = []
+    for k in keys:
+        acc = 0.0
+        for c in range(len(q)):
+            acc += float(q[c]) * float(k[c])
+        scores.append(sm_scale * acc)
+    top = max(scores)
+    weights = [math.exp(s - top) for s in scores]
+    total = sum(weights)
+    out = []
+    for c in range(len(vals[0])):
+        acc = 0.0
+        for w, v in zip(weights, vals):
+            acc += w * float(v[c])
+        out.append(acc / total)
+    return out, top + math.log(total)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_matches_explicit_loop_brute_force(seed):
+    """Tiny extend batch (GQA, page size 2, shuffled pool) against attention
+    written out as loops: each new token of each request walks its visible
+    positions, looks their slots up in the request's page-table row and
+    accumulates over plain Python floats."""
+    spec = Spec("bf_loops", "extend", 2, 4, 2, 4, 2, (0, 6), (1, 4), dtype="fp32")
+    hb = make_host_batch(spec, 70 + seed)
+    lay = hb.layout
+    sm = 0.61
+    o, lse = _run(hb, sm_scale=sm)
+    G = spec.num_q_heads // spec.num_kv_heads
+    for b in range(spec.batch):
+        L = int(lay.seq_lens[b])
+        n = int(lay.new_lens[b])
+        q0 = int(lay.cu_seqlens_q[b])
+        for i in range(n):
+            visible = range(L - n + i + 1)
+            for h in range(spec.num_q_heads):
+                keys = [hb.k_pool[lay.req_to_token[b, j], h // G] for j in visible]
+                vals = [hb.v_pool[lay.req_to_token[b, j], h // G] for j in visible]
+                want, want_lse = _brute_force_row(hb.q[q0 + i, h], keys, vals, sm)
+                np.testing.assert_allclose(o[q0 + i, h], want, rtol=1e-12, atol=1e-13)
+                assert abs(lse[q0 + i, h] - want_lse) < 1e-12
