@@ -1,7 +1,8 @@
 """ctypes binding of libpkv (argument marshalling only).
 
 Each function takes torch tensors that already live on the GPU, checks their
-dtype / shape / contiguity, and forwards raw device pointers and torch's
+dtype, shape (every buffer the kernels write or index against the sizes the
+call implies) and contiguity, and forwards raw device pointers and torch's
 current HIP stream to the C entry point of the same name.  All arithmetic
 runs in the library's kernels; there is no fallback: if ``libpkv.so`` is
 missing, loading fails loudly.
@@ -128,6 +129,33 @@ def _need_rows(t, name, params: Params):
                          f"got {tuple(t.shape)} with {t.element_size()}-byte elements")
 
 
+def _check_q_out_lse(params: Params, q, out, lse, rows: int):
+    """q and out are [rows, Hq, d] and lse, when given, is [rows, Hq]: the
+    kernels write every element of those shapes, so a smaller buffer would be
+    written past its end."""
+    want = (rows, params.num_q_heads, params.head_dim)
+    if tuple(q.shape) != want:
+        raise ValueError(f"q must be {want}, got {tuple(q.shape)}")
+    if out is not None and tuple(out.shape) != want:
+        raise ValueError(f"out must be {want} (the shape of q), got {tuple(out.shape)}")
+    if lse is not None and tuple(lse.shape) != (rows, params.num_q_heads):
+        raise ValueError(f"lse must be {(rows, params.num_q_heads)}, got {tuple(lse.shape)}")
+
+
+def _check_page_table(params: Params, req_to_token, req_pool_indices, batch: int):
+    """Every request has a req_to_token row (directly, or through
+    req_pool_indices) of at least max_kv_len entries."""
+    if req_pool_indices is None:
+        if req_to_token.shape[0] < batch:
+            raise ValueError(f"req_to_token needs a row per request ({batch}) when req_pool_indices is None, "
+                             f"got {req_to_token.shape[0]}")
+    elif req_pool_indices.shape[0] < batch:
+        raise ValueError(f"req_pool_indices needs an entry per request ({batch}), got {req_pool_indices.shape[0]}")
+    if req_to_token.shape[1] < params.max_kv_len:
+        raise ValueError(f"req_to_token rows must hold max_kv_len = {params.max_kv_len} entries, "
+                         f"got {req_to_token.shape[1]}")
+
+
 def workspace_size(params: Params, mode: int, max_batch: int, max_total_q: int = 0) -> Tuple[int, int]:
     lib = load_library()
     ws, sc = _SZ(0), _SZ(0)
@@ -191,6 +219,7 @@ def block_sparse_table(params: Params, seq_lens, req_to_token, blk_indptr, blk_i
     B = seq_lens.shape[0]
     if blk_indptr.shape[0] != B + 1:
         raise ValueError("blk_indptr must have batch + 1 entries")
+    _check_page_table(params, req_to_token, req_pool_indices, B)
     dev = seq_lens.device
     sparse_rtt = torch.empty((B, params.max_kv_len), dtype=torch.int32, device=dev)
     sparse_lens = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -227,8 +256,8 @@ def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan:
     if plan.mode != PKV_DECODE or plan.batch != B:
         raise ValueError("plan was not made by plan_metadata(PKV_DECODE) for this batch")
     n = max(params.decode_q_len, 1)
-    if q.shape[0] != B * n:
-        raise ValueError(f"q must have batch * decode_q_len = {B * n} rows")
+    _check_q_out_lse(params, q, out, lse, B * n)
+    _check_page_table(params, req_to_token, req_pool_indices, B)
     if _is_8bit(params) and sfk is not None:
         nblk = -(-params.max_kv_len // params.k_block)
         if tuple(sfk.shape) != (B, params.num_kv_heads, nblk):
@@ -277,6 +306,10 @@ def attn_extend(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, cu_se
     total_q = q.shape[0]
     if plan.mode != PKV_EXTEND or plan.batch != B or plan.total_q != total_q:
         raise ValueError("plan was not made by plan_metadata(PKV_EXTEND) for this batch and total_q")
+    if cu_seqlens_q.shape[0] != B + 1:
+        raise ValueError(f"cu_seqlens_q must have batch + 1 = {B + 1} entries, got {cu_seqlens_q.shape[0]}")
+    _check_q_out_lse(params, q, out, lse, total_q)
+    _check_page_table(params, req_to_token, req_pool_indices, B)
     if fp8 and sfk is not None:
         nblk = -(-params.max_kv_len // params.k_block)
         if tuple(sfk.shape) != (B, params.num_kv_heads, nblk):

@@ -46,10 +46,13 @@
  *   stream     a hipStream_t passed as void* (NULL = default stream).
  *
  * Ownership and execution: the caller allocates and frees every buffer; the
- * library allocates no device memory and keeps no mutable global state other
- * than the thread-local error text.  Every call validates its host
- * arguments, then enqueues kernels on `stream` and returns without
- * synchronising.  Grids depend only on host arguments, never on device
+ * library allocates no device memory.  Its host-side state is the
+ * thread-local error text and a mutex-guarded cache, per device and kernel
+ * variant, of how many decode work items the device holds at once (an
+ * occupancy query made on the first plan for that device and variant),
+ * which sets how the decode work is cut: results move by rounding only.
+ * Every call validates its host arguments, then enqueues kernels on
+ * `stream` and returns without synchronising.  Grids depend only on host arguments, never on device
  * values, so calls can be captured in a HIP graph.
  *
  * Errors: a non-zero pkv_status means nothing was enqueued (PKV_EHIP: a

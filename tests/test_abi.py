@@ -230,3 +230,39 @@ def test_default_split_target_sizes_for_resident_waves(lib):
         p0 = pkv.Params(hq, hkv, 128, 16, 131073)
         p1 = pkv.Params(hq, hkv, 128, 16, 131073, split_target=4096)
         assert _ws(lib, p0, batch=B) == _ws(lib, p1, batch=B)
+
+
+def _shape_params(n=1):
+    return pkv.Params(8, 2, 128, 16, max_kv_len=64, decode_q_len=n)
+
+
+def test_binding_rejects_q_out_lse_shapes():
+    """Shapes the kernels would write past: out of [B, Hq, d] with several new
+    tokens per request, lse of [B], q with the wrong head count or head_dim."""
+    import torch
+    from flashattention_paged_kv_amd import binding as bd
+    p = _shape_params(n=4)
+    q = torch.empty(3 * 4, 8, 128)
+    bd._check_q_out_lse(p, q, torch.empty(12, 8, 128), torch.empty(12, 8), 12)  # good
+    for q_, out, lse in ((q, torch.empty(3, 8, 128), None),      # out for one token per request
+                         (q, None, torch.empty(12)),                 # lse of [rows]
+                         (q, None, torch.empty(3, 8)),               # lse for one token per request
+                         (torch.empty(12, 4, 128), None, None),      # wrong Hq
+                         (torch.empty(12, 8, 64), None, None),       # wrong d
+                         (torch.empty(3, 8, 128), None, None)):      # q rows
+        with pytest.raises(ValueError):
+            bd._check_q_out_lse(p, q_, out, lse, 12)
+
+
+def test_binding_rejects_short_page_tables():
+    import torch
+    from flashattention_paged_kv_amd import binding as bd
+    p = _shape_params()
+    bd._check_page_table(p, torch.empty(4, 64), None, 4)
+    bd._check_page_table(p, torch.empty(2, 64), torch.empty(4), 4)  # rows reached through the indirection
+    with pytest.raises(ValueError):
+        bd._check_page_table(p, torch.empty(3, 64), None, 4)  # a request without a row
+    with pytest.raises(ValueError):
+        bd._check_page_table(p, torch.empty(4, 64), torch.empty(3), 4)
+    with pytest.raises(ValueError):
+        bd._check_page_table(p, torch.empty(4, 32), None, 4)  # rows shorter than max_kv_len

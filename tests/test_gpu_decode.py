@@ -5,6 +5,7 @@ import math
 import numpy as np
 import pytest
 
+import full_size
 import oracle
 from gpu_util import (assert_bf16_close, assert_lse_close, dev_bf16, dev_i32, host, torch_mod)
 from workloads import SPECS, Spec, make_device_batch, make_host_batch, permute_pages, pool_before_store, round_bf16
@@ -339,46 +340,66 @@ def test_kv_store_skips_slots_outside_the_pool():
     assert np.all(k[lay.new_slots[bad]] == 7.0) and np.all(v[lay.new_slots[bad]] == 7.0)
 
 
-def _sampled_full_size(name, samples, kv_chunk=0):
-    """Full-size workload on the device, in the bench's launch configuration;
-    a sample of (request, head) outputs is recomputed by the oracle one by one."""
+def _full_size(name):
+    """Full-size workload on the device in the bench's launch configuration;
+    every output element and lse is compared with the oracle, run request by
+    request on host copies of the rows each request references."""
     torch = torch_mod()
     pkv = _pkv()
     spec = SPECS[name]
+    n = int(spec.new) if spec.mode == "decode" else 1
     db = make_device_batch(spec, seed=0, layers=1)
     lay = db.layout
     params = pkv.Params(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
-                        max_kv_len=lay.req_to_token.shape[1], kv_chunk=kv_chunk)
+                        max_kv_len=lay.req_to_token.shape[1], decode_q_len=n)
     plan = pkv.plan_metadata(params, pkv.PKV_DECODE, db.seq_lens)
     pkv.kv_store(params, db.k_pools[0], db.v_pools[0], db.k_new[0], db.v_new[0], db.new_slots)
-    lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+    lse = torch.empty((spec.batch * n, spec.num_q_heads), dtype=torch.float32, device="cuda")
     out = pkv.attn_decode(params, db.q, db.k_pools[0], db.v_pools[0], db.req_to_token, db.seq_lens, plan, lse=lse)
     torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all()
-    rng = np.random.default_rng(0)
-    G = spec.num_q_heads // spec.num_kv_heads
-    for _ in range(samples):
-        b = int(rng.integers(0, spec.batch))
-        h = int(rng.integers(0, spec.num_q_heads))
-        L = int(lay.seq_lens[b])
-        rows = db.req_to_token[b, :L].long()
-        g = h // G
-        K = host(db.k_pools[0][rows, g:g + 1])
-        V = host(db.v_pools[0][rows, g:g + 1])
-        q = host(db.q[b:b + 1, h:h + 1])
-        ro, rl = oracle.paged_attention(q, K, V, np.arange(L)[None], [L], [0, 1])
-        assert_bf16_close(host(out[b:b + 1, h:h + 1]), ro, f"{name} b={b} h={h}")
-        assert abs(float(lse[b, h]) - rl[0, 0]) <= 2e-3
+    ro, rl = full_size.decode_reference(db, q_len=n)
+    err, rel = assert_bf16_close(host(out), ro, name)
+    assert_lse_close(lse.cpu().numpy(), rl, name)
+    print(f"{name}: every element of {ro.shape}: max abs {err:.3e}, rel L2 {rel:.3e}", flush=True)
 
 
-def test_full_size_decode_bf16_sampled():
-    _sampled_full_size("decode_bf16", samples=24)
+def test_full_size_decode_bf16_every_element():
+    _full_size("decode_bf16")
 
 
-def test_full_size_long_decode_sampled():
-    _sampled_full_size("long_decode_bf16", samples=6)
+def test_full_size_long_decode_every_element():
+    _full_size("long_decode_bf16")
 
 
-def test_full_size_single_request_decode_sampled():
+def test_full_size_single_request_decode_every_element():
     """One 131k-token request: its 256 splits go through the several-wave merge."""
-    _sampled_full_size("single_decode_bf16", samples=6)
+    _full_size("single_decode_bf16")
+
+
+def test_full_size_decode_n4_every_element():
+    """Four new tokens per request checked in one call, at the full batch."""
+    _full_size("decode_n4_bf16")
+
+
+def test_binding_rejects_wrong_output_shapes_before_any_launch():
+    """out sized for one token per request when each request checks two, lse
+    of [B] instead of [B, Hq], and a page table with fewer rows than requests:
+    each raises ValueError in the binding, before the library is called."""
+    torch = torch_mod()
+    pkv = _pkv()
+    spec = Spec("shapes", "decode", 3, 8, 2, 128, 16, (10, 40), 2)
+    hb = make_host_batch(spec, 90)
+    lay = hb.layout
+    params = pkv.Params(8, 2, 128, 16, max_kv_len=lay.req_to_token.shape[1], decode_q_len=2)
+    seq = dev_i32(lay.seq_lens)
+    plan = pkv.plan_metadata(params, pkv.PKV_DECODE, seq)
+    k_pool, v_pool = dev_bf16(round_bf16(hb.k_pool)), dev_bf16(round_bf16(hb.v_pool))
+    q, rtt = dev_bf16(round_bf16(hb.q)), dev_i32(lay.req_to_token)
+    bad = [dict(out=torch.empty((3, 8, 128), dtype=torch.bfloat16, device="cuda")),
+           dict(lse=torch.empty((3,), dtype=torch.float32, device="cuda"))]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            pkv.attn_decode(params, q, k_pool, v_pool, rtt, seq, plan, **kw)
+    with pytest.raises(ValueError):
+        pkv.attn_decode(params, q, k_pool, v_pool, rtt[:2], seq, plan)
+    torch.cuda.synchronize()

@@ -3,8 +3,10 @@ formula, through the C ABI via the ctypes binding."""
 import numpy as np
 import pytest
 
+import fp8_cases
+import full_size
 import oracle
-from gpu_util import (FP8_REL_L2, dev_f32, dev_i32, dev_qk8, dev_u8, host, kv_dtype_of, qk_codes_of, rel_l2,
+from gpu_util import (FP8_REL_L2, FP8_REL_L2_SAME_MAX, check_rel_l2, dev_f32, dev_i32, dev_qk8, dev_u8, host, kv_dtype_of, qk_codes_of, rel_l2,
                       torch_mod)
 from workloads import SPECS, Spec, make_device_batch, make_host_batch, pool_before_store
 
@@ -59,9 +61,7 @@ def test_fp8_decode_matches_sage_oracle(seed, k_block):
     hb = make_host_batch(replace(SMALL, k_block=k_block), seed)
     o, lse = run_fp8(hb)
     ro, rlse = oracle_fp8(hb)
-    assert np.all(np.isfinite(o))
-    rel = rel_l2(o, ro)
-    assert rel <= FP8_REL_L2, rel
+    check_rel_l2(o, ro, f"decode E4M3 seed={seed} k_block={k_block}")
     assert np.abs(lse - rlse).max() <= 1e-3
 
 
@@ -76,8 +76,7 @@ def test_int8_decode_matches_sage_oracle(seed, k_block):
     hb = make_host_batch(replace(SMALL_I8, k_block=k_block), 40 + seed)
     o, lse = run_fp8(hb)
     ro, rlse = oracle_fp8(hb)
-    assert np.all(np.isfinite(o))
-    assert rel_l2(o, ro) <= FP8_REL_L2, rel_l2(o, ro)
+    check_rel_l2(o, ro, f"decode INT8 seed={seed} k_block={k_block}")
     assert np.abs(lse - rlse).max() <= 1e-3
 
 
@@ -96,7 +95,8 @@ def test_int8_extreme_codes_and_split_merge_with_v_mean():
     o1, l1 = run_fp8(hb, kv_chunk=64, v_mean=vm)
     o2, l2 = run_fp8(hb, v_mean=vm)
     ro, rlse = oracle_fp8(hb, v_mean=vm)
-    assert rel_l2(o1, ro) <= FP8_REL_L2 and rel_l2(o2, ro) <= FP8_REL_L2
+    check_rel_l2(o1, ro, "decode INT8 extreme codes, split")
+    check_rel_l2(o2, ro, "decode INT8 extreme codes")
     assert np.abs(l1 - rlse).max() <= 1e-3 and np.abs(l2 - rlse).max() <= 1e-3
 
 
@@ -109,8 +109,7 @@ def test_int8_several_new_tokens_per_request(n, hq, hkv, kv_chunk, with_vm):
     o, l, sfq_rows = run_fp8_multi(hb, n, v_mean=vm, kv_chunk=kv_chunk)
     ro, rl = oracle.sage_extend(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens,
                                 lay.cu_seqlens_q, sfq_rows, hb.sfk, hb.sfv, spec.k_block, v_mean=vm, qk_codes="int8")
-    assert np.all(np.isfinite(o))
-    assert rel_l2(o, ro) <= FP8_REL_L2, rel_l2(o, ro)
+    check_rel_l2(o, ro, f"decode E4M3 n={n}")
     assert np.abs(l - rl).max() <= 1e-3
 
 
@@ -120,7 +119,8 @@ def test_fp8_split_merge_and_v_mean():
     o1, l1 = run_fp8(hb, kv_chunk=64, v_mean=vm)
     o2, l2 = run_fp8(hb, kv_chunk=4096, v_mean=vm)
     ro, rlse = oracle_fp8(hb, v_mean=vm)
-    assert rel_l2(o1, ro) <= FP8_REL_L2 and rel_l2(o2, ro) <= FP8_REL_L2
+    check_rel_l2(o1, ro, "decode E4M3 split, v_mean")
+    check_rel_l2(o2, ro, "decode E4M3 unsplit, v_mean")
     assert np.abs(l1 - rlse).max() <= 1e-3
 
 
@@ -135,7 +135,7 @@ def test_fp8_many_segments_and_empty_requests_with_v_mean():
     vm = np.random.default_rng(1).uniform(-1, 1, size=hb.sfv.shape).astype(np.float32)
     o, lse = run_fp8(hb, v_mean=vm, split_target=6, seq_lens=seq)
     ro, rlse = oracle_fp8(hb, v_mean=vm, seq_lens=seq)
-    assert rel_l2(o, ro) <= FP8_REL_L2
+    check_rel_l2(o, ro, "decode E4M3 many segments")
     fin = np.isfinite(rlse)
     assert np.array_equal(np.isfinite(lse), fin)
     assert np.abs(lse[fin] - rlse[fin]).max() <= 1e-3
@@ -154,13 +154,13 @@ def test_fp8_constant_scores_closed_form():
     for b in range(SMALL.batch):
         L = int(lay.seq_lens[b])
         np.testing.assert_allclose(lse[b], np.log(L), rtol=0, atol=1e-5)
-    assert rel_l2(o, ro) <= 4e-3  # only bf16 output rounding and fp32 sums remain
+    check_rel_l2(o, ro, "decode E4M3 constant scores", bound=FP8_REL_L2_SAME_MAX)
 
 
 @pytest.mark.parametrize("name", ["decode_fp8", "decode_int8"])
-def test_full_size_8bit_decode_sampled(name):
+def test_full_size_8bit_decode_every_element(name):
     """The full 8-bit decode workloads (E4M3, and INT8 Q/K) in the bench's
-    launch configuration, 24 sampled requests recomputed by the oracle."""
+    launch configuration; every output element and lse against the oracle."""
     torch = torch_mod()
     pkv = _pkv()
     spec = SPECS[name]
@@ -171,25 +171,13 @@ def test_full_size_8bit_decode_sampled(name):
                         q_block=spec.q_block, k_block=spec.k_block)
     plan = pkv.plan_metadata(params, pkv.PKV_DECODE, db.seq_lens)
     pkv.kv_store(params, db.k_pools[0], db.v_pools[0], db.k_new[0], db.v_new[0], db.new_slots)
-    out = pkv.attn_decode(params, db.q, db.k_pools[0], db.v_pools[0], db.req_to_token, db.seq_lens, plan,
+    lse = torch.empty((spec.batch, spec.num_q_heads), dtype=torch.float32, device="cuda")
+    out = pkv.attn_decode(params, db.q, db.k_pools[0], db.v_pools[0], db.req_to_token, db.seq_lens, plan, lse=lse,
                           sfq=db.sfq, sfk=db.sfk, sfv=db.sfv)
     torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all()
-    rng = np.random.default_rng(0)
-    got, ref = [], []
-    for _ in range(24):
-        b = int(rng.integers(0, spec.batch))
-        L = int(lay.seq_lens[b])
-        rows = db.req_to_token[b, :L].long()
-        q8 = db.q[b:b + 1].cpu().numpy()
-        k8 = db.k_pools[0][rows].cpu().numpy()
-        v8 = db.v_pools[0][rows].cpu().numpy()
-        o, _ = oracle.sage_decode(q8, k8, v8, np.arange(L)[None], [L], db.sfq[b:b + 1].cpu().numpy(),
-                                  db.sfk[b:b + 1].cpu().numpy(), db.sfv[b:b + 1].cpu().numpy(), spec.k_block,
-                                  qk_codes=qk_codes_of(spec))
-        got.append(host(out[b:b + 1]))
-        ref.append(o)
-        assert rel_l2(got[-1], o) <= FP8_REL_L2, b
+    ro, rl = full_size.decode_reference(db, sage=True, qk_codes=qk_codes_of(spec))
+    check_rel_l2(host(out), ro, f"{name} every element of {ro.shape}")
+    assert np.abs(lse.cpu().numpy() - rl).max() <= 1e-3
 
 
 def run_fp8_multi(hb, n, v_mean=None, kv_chunk=0, seed=None):
@@ -234,6 +222,59 @@ def test_fp8_several_new_tokens_per_request(n, hq, hkv, kv_chunk, with_vm):
     o, l, sfq_rows = run_fp8_multi(hb, n, v_mean=vm, kv_chunk=kv_chunk)
     ro, rl = oracle.sage_extend(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens,
                                 lay.cu_seqlens_q, sfq_rows, hb.sfk, hb.sfv, spec.k_block, v_mean=vm)
-    assert np.all(np.isfinite(o))
-    assert rel_l2(o, ro) <= FP8_REL_L2, rel_l2(o, ro)
+    check_rel_l2(o, ro, f"decode E4M3 n={n}")
     assert np.abs(l - rl).max() <= 1e-3
+
+
+# two to eight keys per request: few keys, so each request's E4M3 rounding of
+# P does not average out and the quantisation step moves O by about 2%
+SHORT = Spec("f8_short", "decode", 64, 32, 8, 128, 16, (1, 7), 1, dtype="fp8", k_block=16)
+TIGHT_CASES = {"e4m3_kb64": SMALL, "e4m3_kb16": Spec("f8_small16", "decode", 6, 32, 8, 128, 16, (0, 700), 1,
+                                                     dtype="fp8", k_block=16),
+               "int8_kb64": SMALL_I8, "e4m3_short": SHORT,
+               "int8_short": Spec("i8_short", "decode", 64, 32, 8, 128, 16, (1, 7), 1, dtype="int8", k_block=16)}
+
+
+@pytest.mark.parametrize("case", sorted(TIGHT_CASES))
+def test_8bit_decode_tight_when_the_row_max_is_first(case):
+    """Every row's maximum at position 0 and one segment per request: the
+    kernel's running max is the oracle's row max from the first tile on, so
+    its E4M3 codes of P are the oracle's and the bound is the bf16 rounding of
+    O.  (On the short requests, rounding p before scaling by 448 moves the
+    oracle's O by about 2% and dividing by the codes' sum by about 0.9%.)"""
+    spec = TIGHT_CASES[case]
+    hb = make_host_batch(spec, 60)
+    gap = fp8_cases.put_row_max_first(hb, qk_codes_of(spec))
+    assert gap > 0
+    o, lse = run_fp8(hb, kv_chunk=4096, sm_scale=0.03)
+    ro, rlse = oracle_fp8(hb, sm_scale=0.03)
+    check_rel_l2(o, ro, f"decode {case}, row max first", bound=FP8_REL_L2_SAME_MAX)
+    assert np.abs(lse - rlse).max() <= 1e-4
+
+
+@pytest.mark.parametrize("n", [2, 4])
+def test_8bit_multi_token_decode_tight_when_the_row_max_is_first(n):
+    """The same bound for several new tokens per request in one call: every
+    new row sees position 0."""
+    spec = Spec("f8_multi_tight", "decode", 5, 32, 8, 128, 16, (0, 900), n, dtype="fp8", k_block=64)
+    hb = make_host_batch(spec, 62 + n)
+    lay = hb.layout
+    rng = np.random.default_rng(n)
+    sfq_rows = (hb.sfq[np.repeat(np.arange(spec.batch), n)] * rng.uniform(0.8, 1.25, (spec.batch * n, 32)))
+    hb.sfq = sfq_rows.astype(np.float32)  # one scale per row: the multi-token decode reads [B*n, Hq]
+    fp8_cases.put_row_max_first(hb, "e4m3")
+    torch = torch_mod()
+    pkv = _pkv()
+    k_pool = dev_u8(pool_before_store(hb.k_codes, lay.new_slots, fill=0x7F))
+    v_pool = dev_u8(pool_before_store(hb.v_codes, lay.new_slots, fill=0x7F))
+    params = pkv.Params(32, 8, 128, 16, max_kv_len=lay.req_to_token.shape[1], kv_dtype=pkv.PKV_FP8_E4M3,
+                        q_block=1, k_block=64, kv_chunk=4096, decode_q_len=n)
+    seq = dev_i32(lay.seq_lens)
+    plan = pkv.plan_metadata(params, pkv.PKV_DECODE, seq)
+    pkv.kv_store(params, k_pool, v_pool, dev_u8(hb.k_new_codes), dev_u8(hb.v_new_codes), dev_i32(lay.new_slots))
+    out = pkv.attn_decode(params, dev_u8(hb.q_codes), k_pool, v_pool, dev_i32(lay.req_to_token), seq, plan,
+                          sm_scale=0.03, sfq=dev_f32(hb.sfq), sfk=dev_f32(hb.sfk), sfv=dev_f32(hb.sfv))
+    torch.cuda.synchronize()
+    ro, _ = oracle.sage_extend(hb.q_codes, hb.k_codes, hb.v_codes, lay.req_to_token, lay.seq_lens, lay.cu_seqlens_q,
+                               hb.sfq, hb.sfk, hb.sfv, 64, sm_scale=0.03)
+    check_rel_l2(host(out), ro, f"decode E4M3 n={n}, row max first", bound=FP8_REL_L2_SAME_MAX)
