@@ -23,7 +23,8 @@ PKV_BF16, PKV_FP8_E4M3, PKV_SAGE_INT8 = 0, 1, 2
 PKV_DECODE, PKV_EXTEND = 0, 1
 
 EXPORTED = ("pkv_workspace_size", "pkv_plan_metadata", "pkv_kv_store", "pkv_block_sparse_table",
-            "pkv_attn_decode", "pkv_attn_extend", "pkv_last_error", "pkv_version")
+            "pkv_attn_decode", "pkv_attn_decode_noalloc", "pkv_attn_extend", "pkv_last_error", "pkv_version")
+STATIC_SCRATCH_BYTES = 32 << 20  # PKV_STATIC_SCRATCH_BYTES
 
 
 class PkvError(RuntimeError):
@@ -68,10 +69,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_block_sparse_table.argtypes = [pp, _I32, _P, _P, _I64, _P, _P, _P, _I64, _I32, _P, _P, _P, _P, _P]
     lib.pkv_attn_decode.argtypes = [pp, _P, _P, _P, _P, _P, _I64, _P, _I64, _P, _P, _I32, _F,
                                     _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]
+    lib.pkv_attn_decode_noalloc.argtypes = [pp, _P, _P, _P, _P, _P, _I64, _P, _I64, _P, _P, _I32, _F,
+                                            _P, _P, _P, _P, _P, _SZ, _P]
     lib.pkv_attn_extend.argtypes = [pp, _P, _P, _P, _P, _P, _I64, _P, _I64, _P, _P, _P, _I32, _I64,
                                     _F, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]
     for f in ("pkv_workspace_size", "pkv_plan_metadata", "pkv_kv_store", "pkv_block_sparse_table",
-              "pkv_attn_decode", "pkv_attn_extend", "pkv_version"):
+              "pkv_attn_decode", "pkv_attn_decode_noalloc", "pkv_attn_extend", "pkv_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []
@@ -242,6 +245,25 @@ def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan:
                 sfq=None, sfk=None, sfv=None, v_mean=None):
     """Decode attention: q [B, Hq, d] (bf16, uint8 E4M3 codes, or int8 codes for PKV_SAGE_INT8)
     -> out [B, Hq, d] bf16."""
+    return _attn_decode(params, q, k_pool, v_pool, req_to_token, seq_lens, plan, scratch, out, lse, sm_scale,
+                        req_pool_indices, sfq, sfk, sfv, v_mean, noalloc=False)
+
+
+def attn_decode_noalloc(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan: Plan, out,
+                        lse=None, sm_scale: Optional[float] = None, req_pool_indices=None,
+                        sfq=None, sfk=None, sfv=None, v_mean=None):
+    """``pkv_attn_decode_noalloc``: the decode of :func:`attn_decode` with its
+    split partials in the library's static device scratch; ``out`` must be
+    given (nothing is allocated here or in the library).  Calls that overlap
+    on one GPU race on that scratch."""
+    if out is None:
+        raise ValueError("attn_decode_noalloc writes into a caller's out buffer; pass out=")
+    return _attn_decode(params, q, k_pool, v_pool, req_to_token, seq_lens, plan, None, out, lse, sm_scale,
+                        req_pool_indices, sfq, sfk, sfv, v_mean, noalloc=True)
+
+
+def _attn_decode(params, q, k_pool, v_pool, req_to_token, seq_lens, plan, scratch, out, lse, sm_scale,
+                 req_pool_indices, sfq, sfk, sfv, v_mean, noalloc):
     import torch
     qt = {PKV_FP8_E4M3: torch.uint8, PKV_SAGE_INT8: torch.int8}.get(params.kv_dtype, torch.bfloat16)
     _need(q, "q", qt, 3)
@@ -271,12 +293,18 @@ def attn_decode(params: Params, q, k_pool, v_pool, req_to_token, seq_lens, plan:
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, 3)
-    if scratch is None:
+    if scratch is None and not noalloc:
         scratch = torch.empty(max(plan.scratch_bytes, 16), dtype=torch.uint8, device=q.device)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(params.head_dim)
     lib = load_library()
     ws = plan.workspace
+    if noalloc:
+        _check(lib.pkv_attn_decode_noalloc(
+            ctypes.byref(params), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+            _ptr(req_to_token), req_to_token.shape[1], _ptr(req_pool_indices), _ptr(seq_lens), B, float(sm_scale),
+            _ptr(sfq), _ptr(sfk), _ptr(sfv), _ptr(v_mean), _ptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+        return out
     _check(lib.pkv_attn_decode(ctypes.byref(params), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                k_pool.shape[0], _ptr(req_to_token), req_to_token.shape[1], _ptr(req_pool_indices),
                                _ptr(seq_lens), B, float(sm_scale), _ptr(sfq), _ptr(sfk), _ptr(sfv), _ptr(v_mean),

@@ -255,12 +255,19 @@ int pkv_kv_store(const pkv_params* params, void* k_pool, void* v_pool, int64_t p
                       "kv_store launch");
 }
 
-int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void* q, const void* k_pool,
-                    const void* v_pool, int64_t pool_slots, const int32_t* req_to_token, int64_t rtt_stride,
-                    const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch, float sm_scale,
-                    const float* sfq, const float* sfk, const float* sfv, const float* v_mean,
-                    const void* workspace, size_t workspace_bytes, void* scratch, size_t scratch_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by pkv_attn_decode (caller's scratch) and pkv_attn_decode_noalloc
+// (the static scratch): with static_scratch set, `scratch` is ignored and the
+// static array serves if it is large enough.
+int attn_decode_impl(const pkv_params* params, void* out, float* lse, const void* q, const void* k_pool,
+                     const void* v_pool, int64_t pool_slots, const int32_t* req_to_token, int64_t rtt_stride,
+                     const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch, float sm_scale,
+                     const float* sfq, const float* sfk, const float* sfv, const float* v_mean,
+                     const void* workspace, size_t workspace_bytes, void* scratch, size_t scratch_bytes,
+                     bool static_scratch, void* stream) {
   if (int rc = check_params(params, PKV_DECODE)) return rc;
   if (batch < 0) return fail(PKV_EINVAL, "batch=%d must be >= 0", batch);
   if (pool_slots < 1 || pool_slots > ((int64_t)1 << 31))
@@ -288,6 +295,18 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
     return fail(PKV_EWORKSPACE, "workspace_bytes=%zu is smaller than the %lld bytes required", workspace_bytes,
                 (long long)(w.total_ints * 4));
   const pkv::DecodeScratch sc = pkv::decode_scratch(*params, batch, tgt);
+  if (static_scratch) {
+    if (sc.total_bytes > pkv::kStaticScratchBytes)
+      return fail(PKV_EWORKSPACE,
+                  "this decode needs %lld bytes of split scratch; the static scratch holds %lld "
+                  "(use pkv_attn_decode with a caller buffer)",
+                  (long long)sc.total_bytes, (long long)pkv::kStaticScratchBytes);
+    void* p = nullptr;
+    const hipError_t e = pkv::static_scratch_address(&p);
+    if (e != hipSuccess) return fail(PKV_EHIP, "static scratch address: %s", hipGetErrorString(e));
+    scratch = p;
+    scratch_bytes = (size_t)pkv::kStaticScratchBytes;
+  }
   if (!scratch || (int64_t)scratch_bytes < sc.total_bytes)
     return fail(PKV_EWORKSPACE, "scratch_bytes=%zu is smaller than the %lld bytes required", scratch ? scratch_bytes : 0,
                 (long long)sc.total_bytes);
@@ -331,6 +350,31 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
                      : pkv::launch_decode_bf16(a, params->head_dim, w.capacity, batch, s);
   if (e != hipSuccess) return check_launch(e, "attn_decode launch");
   return check_launch(pkv::launch_decode_merge(a, params->head_dim, w.capacity, batch, s), "attn_decode merge launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void* q, const void* k_pool,
+                    const void* v_pool, int64_t pool_slots, const int32_t* req_to_token, int64_t rtt_stride,
+                    const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch, float sm_scale,
+                    const float* sfq, const float* sfk, const float* sfv, const float* v_mean,
+                    const void* workspace, size_t workspace_bytes, void* scratch, size_t scratch_bytes,
+                    void* stream) {
+  return attn_decode_impl(params, out, lse, q, k_pool, v_pool, pool_slots, req_to_token, rtt_stride,
+                          req_pool_indices, seq_lens, batch, sm_scale, sfq, sfk, sfv, v_mean, workspace,
+                          workspace_bytes, scratch, scratch_bytes, false, stream);
+}
+
+int pkv_attn_decode_noalloc(const pkv_params* params, void* out, float* lse, const void* q, const void* k_pool,
+                            const void* v_pool, int64_t pool_slots, const int32_t* req_to_token,
+                            int64_t rtt_stride, const int32_t* req_pool_indices, const int32_t* seq_lens,
+                            int32_t batch, float sm_scale, const float* sfq, const float* sfk, const float* sfv,
+                            const float* v_mean, const void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_decode_impl(params, out, lse, q, k_pool, v_pool, pool_slots, req_to_token, rtt_stride,
+                          req_pool_indices, seq_lens, batch, sm_scale, sfq, sfk, sfv, v_mean, workspace,
+                          workspace_bytes, nullptr, 0, true, stream);
 }
 
 int pkv_attn_extend(const pkv_params* params, void* out, float* lse, const void* q, const void* k_pool,

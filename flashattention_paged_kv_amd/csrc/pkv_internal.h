@@ -14,6 +14,7 @@ namespace pkv {
 constexpr int kDecodeTile = 32;       // decode tokens per inner step (two 16-token MFMA blocks)
 // Resident decode waves assumed when no device can be queried (256 CUs x 16).
 constexpr int kFallbackResidentWaves = 4096;
+constexpr int64_t kStaticScratchBytes = PKV_STATIC_SCRATCH_BYTES;  // static decode scratch per device
 constexpr int kExtendRows = 256;      // (head, token) rows per extend work item (8 waves x 32)
 constexpr int kExtendTileN = 64;      // keys per extend inner step
 constexpr int kPlanThreads = 1024;
@@ -216,6 +217,9 @@ struct SparseTableArgs {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_block_sparse_table(const SparseTableArgs& a, int32_t batch, hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+// Device address of the static decode scratch on the current device (looked
+// up on the first call per device).
+hipError_t static_scratch_address(void** ptr);
 hipError_t launch_extend_fp8(const ExtendArgs& a, int64_t capacity, hipStream_t s);
 hipError_t launch_kv_store(void* k_pool, void* v_pool, int64_t pool_slots, const void* k_new,
                            const void* v_new, const int32_t* slots, int64_t num_tokens,

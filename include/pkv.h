@@ -46,7 +46,8 @@
  *   stream     a hipStream_t passed as void* (NULL = default stream).
  *
  * Ownership and execution: the caller allocates and frees every buffer; the
- * library allocates no device memory.  Its host-side state is the
+ * library allocates no device memory (its code object carries one static
+ * scratch array per device, used only by pkv_attn_decode_noalloc).  Its host-side state is the
  * thread-local error text and a mutex-guarded cache, per device and kernel
  * variant, of how many decode work items the device holds at once (an
  * occupancy query made on the first plan for that device and variant),
@@ -196,6 +197,30 @@ int pkv_attn_decode(const pkv_params* params, void* out, float* lse, const void*
                     const float* sfk, const float* sfv, const float* v_mean,
                     const void* workspace, size_t workspace_bytes, void* scratch,
                     size_t scratch_bytes, void* stream);
+
+/* Largest split scratch pkv_attn_decode_noalloc can serve (32 MiB). */
+#define PKV_STATIC_SCRATCH_BYTES (32ll << 20)
+
+/* DECODE without a scratch buffer, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, results and errors are those of
+ * pkv_attn_decode, whose kernels it runs; the split partials go to a static
+ * device array of PKV_STATIC_SCRATCH_BYTES that the library's code object
+ * holds on every GPU it runs on until the process ends (its address is
+ * looked up once per device, on the first call with that device current).
+ * A decode whose scratch_bytes (pkv_workspace_size) exceeds that size is
+ * rejected with PKV_EWORKSPACE.  The call allocates and frees nothing.  Every
+ * call on one GPU shares that GPU's array and no part of it needs clearing
+ * (the split kernel writes every partial the merge reads), so calls that
+ * overlap on one GPU (different streams, or host threads) race and give
+ * wrong results: serialise them, e.g. on one stream. */
+int pkv_attn_decode_noalloc(const pkv_params* params, void* out, float* lse, const void* q,
+                            const void* k_pool, const void* v_pool, int64_t pool_slots,
+                            const int32_t* req_to_token, int64_t rtt_stride,
+                            const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t batch,
+                            float sm_scale, const float* sfq, const float* sfk, const float* sfv,
+                            const float* v_mean, const void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* EXTEND: causal attention of the total_q new-token rows (q: [total_q, Hq, d],
  * out: [total_q, Hq, d] bf16) over their request's cached prefix and
