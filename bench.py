@@ -36,6 +36,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -163,6 +165,44 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "kernel": "torch.neg (bf16 elementwise)"}), flush=True)
 
 
+# ---------------------------------------------------------------- oracle timing (cpu_baseline)
+def _rows_host(pool, rows):
+    """Pool rows [L, Hkv, d] of one request, copied to the host: float32 for
+    bf16 pools (exact), the raw codes for 8-bit pools."""
+    import torch
+    t = pool[rows]
+    return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+
+
+def _q_host(q):
+    import torch
+    return (q.float() if q.dtype == torch.bfloat16 else q).cpu().numpy()
+
+
+def time_oracle(units, budget_s):
+    """Run ``units`` (an iterator of (prepare, run, work) triples: prepare
+    copies a unit's inputs to the host and is not timed, run is one oracle
+    call) until ``budget_s`` seconds of oracle time are spent.  Returns
+    (work done, oracle seconds, units run)."""
+    done, spent, n = 0, 0.0, 0
+    for prepare, run, work in units:
+        args = prepare()
+        t0 = time.perf_counter()
+        run(*args)
+        spent += time.perf_counter() - t0
+        done += work
+        n += 1
+        if spent >= budget_s:
+            break
+    return done, spent, n
+
+
+def _cycle(seq):
+    while True:
+        for x in seq:
+            yield x
+
+
 # ---------------------------------------------------------------- workloads
 KV_DTYPE_NAMES = {"bf16": "bf16", "fp8": "fp8_e4m3", "int8": "int8 q/k (sage), fp8_e4m3 v"}
 
@@ -231,37 +271,37 @@ class DecodeRunner:
                 "algorithmic_bytes_per_launch": self.kv_bytes_per_layer,
                 "avg_launch_us": round(avg_launch_s * 1e6, 2)}
 
-    def cpu_baseline(self, budget_s, oracle):
-        """The fp64 oracle on layer 0 of the same batch, request by request until the budget is spent."""
-        import numpy as np
-        torch, db, spec = self.torch, self.db, self.spec
+    def _oracle_units(self, oracle):
+        """One unit per request of layer 0: all heads of its new-token rows."""
+        db, spec = self.db, self.spec
         lay = db.layout
-        if self.fp8:
-            q = db.q.cpu().numpy()
-            kp = db.k_pools[0].cpu().numpy()
-            vp = db.v_pools[0].cpu().numpy()
-            sfq, sfk, sfv = db.sfq.cpu().numpy(), db.sfk.cpu().numpy(), db.sfv.cpu().numpy()
-        else:
-            q = db.q.float().cpu().numpy()
-            kp = db.k_pools[0].float().cpu().numpy()
-            vp = db.v_pools[0].float().cpu().numpy()
-        done_bytes, n = 0, 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:  # whole passes over the batch, then a partial one
-            b = n % spec.batch
-            rtt = lay.req_to_token[b:b + 1]
-            L = lay.seq_lens[b:b + 1]
+        q = _q_host(db.q)
+        sc = [t.cpu().numpy() for t in (db.sfq, db.sfk, db.sfv)] if self.fp8 else None
+        esize = 1 if self.fp8 else 2
+        nq = self.q_len
+
+        def unit(b):
+            L = int(lay.seq_lens[b])
+            rows = db.req_to_token[b, :L].long()
+            prepare = lambda: (_rows_host(db.k_pools[0], rows), _rows_host(db.v_pools[0], rows))
+            rtt = np.arange(L)[None]
             if self.fp8:
-                oracle.sage_decode(q[b:b + 1], kp, vp, rtt, L, sfq[b:b + 1], sfk[b:b + 1], sfv[b:b + 1],
-                                   k_block=spec.k_block, qk_codes=self.qk_codes)
+                run = lambda K, V: oracle.sage_decode(q[b:b + 1], K, V, rtt, [L], sc[0][b:b + 1], sc[1][b:b + 1],
+                                                      sc[2][b:b + 1], k_block=spec.k_block, qk_codes=self.qk_codes)
             else:
-                nq = self.q_len
-                oracle.paged_attention(q[b * nq:(b + 1) * nq], kp, vp, rtt, L, [0, nq])
-            done_bytes += int(L[0]) * spec.num_kv_heads * spec.head_dim * 2 * (1 if self.fp8 else 2)
-            n += 1
-        dt = time.perf_counter() - t0
-        return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "seconds": round(dt, 2),
-                "sample": f"layer 0 of {spec.name}: {n} request-attentions ({n / spec.batch:.1f} passes over "
+                run = lambda K, V: oracle.paged_attention(q[b * nq:(b + 1) * nq], K, V, rtt, [L], [0, nq])
+            return prepare, run, L * spec.num_kv_heads * spec.head_dim * 2 * esize
+
+        return (unit(b) for b in _cycle(range(spec.batch)))
+
+    def cpu_baseline(self, budget_s, oracle):
+        """The fp64 oracle on layer 0 of the same batch, request by request
+        (each request's rows gathered on the device and copied to the host
+        untimed) until ``budget_s`` seconds of oracle time are spent."""
+        spec = self.spec
+        done, dt, n = time_oracle(self._oracle_units(oracle), budget_s)
+        return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "seconds": round(dt, 2),
+                "sample": f"layer 0 of {spec.name}: {n} request-attentions ({n / spec.batch:.2f} passes over "
                           f"the {spec.batch}-request batch), all {spec.num_q_heads} heads, fp64"}
 
 
@@ -308,35 +348,47 @@ class SparseDecodeRunner(DecodeRunner):
                   "selected_tokens": self.selected_tokens})
         return d
 
-    def cpu_baseline(self, budget_s, oracle):
-        """The fp64 block-sparse oracle on layer 0, request by request until the budget is spent."""
+    def _oracle_units(self, oracle):
+        """One unit per (request, kv head) of layer 0: that head's query heads
+        over the request's listed blocks (a whole 40-head request of this
+        workload takes the 8-bit oracle tens of seconds)."""
         db, spec = self.db, self.spec
         lay = db.layout
-        if self.fp8:
-            q, kp, vp = db.q.cpu().numpy(), db.k_pools[0].cpu().numpy(), db.v_pools[0].cpu().numpy()
-            sfq, sfk, sfv = db.sfq.cpu().numpy(), db.sfk.cpu().numpy(), db.sfv.cpu().numpy()
-        else:
-            q, kp, vp = (t.float().cpu().numpy() for t in (db.q, db.k_pools[0], db.v_pools[0]))
+        q = _q_host(db.q)
+        sc = [t.cpu().numpy() for t in (db.sfq, db.sfk, db.sfv)] if self.fp8 else None
         bs = spec.sparse_block
-        done_bytes, n = 0, 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            b = n % spec.batch
+        esize = 1 if self.fp8 else 2
+        G = spec.num_q_heads // spec.num_kv_heads
+
+        def unit(b, g):
+            L = int(lay.seq_lens[b])
+            rows = db.req_to_token[b, :L].long()
             blocks = lay.blk_indices[lay.blk_indptr[b]:lay.blk_indptr[b + 1]]
             ip = [0, len(blocks)]
-            rtt, L = lay.req_to_token[b:b + 1], lay.seq_lens[b:b + 1]
+            rtt = np.arange(L)[None]
+            hs = slice(g * G, (g + 1) * G)
+            prepare = lambda: (_rows_host(db.k_pools[0][:, g:g + 1], rows), _rows_host(db.v_pools[0][:, g:g + 1], rows))
             if self.fp8:
-                oracle.block_sparse_sage_decode(q[b:b + 1], kp, vp, rtt, L, ip, blocks, bs, sfq[b:b + 1],
-                                                sfk[b:b + 1], sfv[b:b + 1], spec.k_block, qk_codes=self.qk_codes)
+                run = lambda K, V: oracle.block_sparse_sage_decode(q[b:b + 1, hs], K, V, rtt, [L], ip, blocks, bs,
+                                                                   sc[0][b:b + 1, hs], sc[1][b:b + 1, g:g + 1],
+                                                                   sc[2][b:b + 1, g:g + 1], spec.k_block,
+                                                                   qk_codes=self.qk_codes)
             else:
-                oracle.block_sparse_decode(q[b:b + 1], kp, vp, rtt, L, ip, blocks, bs)
-            sel = sum(max(0, min(bs, int(L[0]) - int(k) * bs)) for k in blocks)
-            done_bytes += sel * spec.num_kv_heads * spec.head_dim * 2 * (1 if self.fp8 else 2)
-            n += 1
-        dt = time.perf_counter() - t0
-        return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "seconds": round(dt, 2),
-                "sample": f"layer 0 of {spec.name}: {n} request-attentions over the listed blocks, "
-                          f"all {spec.num_q_heads} heads, fp64"}
+                run = lambda K, V: oracle.block_sparse_decode(q[b:b + 1, hs], K, V, rtt, [L], ip, blocks, bs)
+            sel = sum(max(0, min(bs, L - int(k) * bs)) for k in blocks)
+            return prepare, run, sel * spec.head_dim * 2 * esize
+
+        order = [(b, g) for b in range(spec.batch) for g in range(spec.num_kv_heads)]
+        return (unit(b, g) for b, g in _cycle(order))
+
+    def cpu_baseline(self, budget_s, oracle):
+        """The fp64 block-sparse oracle on layer 0, request by request, until
+        ``budget_s`` seconds of oracle time are spent."""
+        spec = self.spec
+        done, dt, n = time_oracle(self._oracle_units(oracle), budget_s)
+        return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "seconds": round(dt, 2),
+                "sample": f"layer 0 of {spec.name}: {n} (request, kv head) attentions over the request's "
+                          f"listed blocks ({n / spec.num_kv_heads:.2f} requests' worth, all heads), fp64"}
 
 
 class ExtendRunner:
@@ -396,6 +448,48 @@ class ExtendRunner:
                 "frac": round(achieved / peak, 4), "traffic": traffic_from_counters(workload),
                 "kernel": "extend_fp8_kernel" if self.fp8 else "extend_bf16_kernel",
                 "algorithmic_flops_per_launch": self.flops_per_layer, "avg_launch_us": round(avg_launch_s * 1e6, 2)}
+
+    def _oracle_units(self, oracle):
+        """bf16: one unit per request of layer 0 (every new-token row, all
+        heads).  8-bit: one unit per new-token row (all heads over its
+        visible keys, through the decode form of the formula), since the
+        oracle's per-row loop makes a whole request take minutes."""
+        db, spec = self.db, self.spec
+        lay = db.layout
+        q = _q_host(db.q)
+        d, hq = spec.head_dim, spec.num_q_heads
+        cu = lay.cu_seqlens_q
+        if not self.fp8:
+            def unit(b):
+                L, n = int(lay.seq_lens[b]), int(cu[b + 1] - cu[b])
+                rows = db.req_to_token[b, :L].long()
+                prepare = lambda: (_rows_host(db.k_pools[0], rows), _rows_host(db.v_pools[0], rows))
+                run = lambda K, V: oracle.paged_attention(q[cu[b]:cu[b + 1]], K, V, np.arange(L)[None], [L], [0, n])
+                p = L - n
+                return prepare, run, 4 * d * hq * (n * p + n * (n + 1) // 2)
+            return (unit(b) for b in _cycle(range(spec.batch)))
+        sfq, sfk, sfv = (t.cpu().numpy() for t in (db.sfq, db.sfk, db.sfv))
+
+        def row_unit(b, t):
+            L, n = int(lay.seq_lens[b]), int(cu[b + 1] - cu[b])
+            vis = L - n + (t - int(cu[b])) + 1
+            rows = db.req_to_token[b, :vis].long()
+            prepare = lambda: (_rows_host(db.k_pools[0], rows), _rows_host(db.v_pools[0], rows))
+            run = lambda K, V: oracle.sage_decode(q[t:t + 1], K, V, np.arange(vis)[None], [vis], sfq[t:t + 1],
+                                                  sfk[b:b + 1], sfv[b:b + 1], spec.k_block)
+            return prepare, run, 4 * d * hq * vis
+
+        order = [(b, t) for b in range(spec.batch) for t in range(int(cu[b]), int(cu[b + 1]), 97)]
+        return (row_unit(b, t) for b, t in _cycle(order))
+
+    def cpu_baseline(self, budget_s, oracle):
+        spec = self.spec
+        done, dt, n = time_oracle(self._oracle_units(oracle), budget_s)
+        what = (f"{n} requests (every new-token row, all {spec.num_q_heads} heads)" if not self.fp8 else
+                f"{n} new-token rows (every 97th row of each request, all {spec.num_q_heads} heads over its "
+                "visible keys)")
+        return {"value": round(done / dt / 1e12, 6), "unit": "TFLOP/s", "seconds": round(dt, 2),
+                "sample": f"layer 0 of {spec.name}: {what}, fp64; unmasked flops"}
 
 
 RUNNERS = {"decode_bf16": DecodeRunner, "long_decode_bf16": DecodeRunner, "single_decode_bf16": DecodeRunner,
@@ -462,6 +556,54 @@ def measure(name, steps, warmup, layers, torch, pkv, workloads, graph=False):
     return runner, ms, value, runner.roofline(avg_launch_s, name)
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
+def cpu_baseline_of(runner, budget_s):
+    """The oracle timed on the host cores on a bounded sample of the runner's workload."""
+    import oracle
+    cb = runner.cpu_baseline(budget_s, oracle)
+    cb.update({"cores": _blas_threads(), "kind": "oracle"})
+    return cb
+
+
+def single_thread_baselines(runner, budget_s):
+    """The oracle with its BLAS pool limited to one thread: on the headline
+    batch (same sample rule) and on the tiny decode and extend batches (whole
+    batch per call, repeated until the budget is spent)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import workloads
+    out = {}
+    with threadpool_limits(limits=1):
+        cb = runner.cpu_baseline(budget_s, oracle)
+        cb.update({"cores": 1, "kind": "oracle"})
+        out[runner.spec.name] = cb
+        for name in ("tiny_decode", "tiny_extend"):
+            hb = workloads.make_host_batch(workloads.SPECS[name], 0)
+            lay, spec = hb.layout, hb.layout.spec
+            q, kp, vp = (workloads.round_bf16(x) for x in (hb.q, hb.k_pool, hb.v_pool))
+            n = lay.new_lens.astype("int64")
+            p = lay.prefix_lens.astype("int64")
+            if spec.mode == "decode":
+                work, unit = int(lay.seq_lens.astype("int64").sum()) * spec.num_kv_heads * spec.head_dim * 2 * 2, "GB/s"
+            else:
+                work, unit = 4 * spec.head_dim * spec.num_q_heads * int((n * p + n * (n + 1) // 2).sum()), "TFLOP/s"
+            run = lambda: oracle.paged_attention(q, kp, vp, lay.req_to_token, lay.seq_lens, lay.cu_seqlens_q)
+            done, dt, calls = time_oracle(((lambda: (), run, work) for _ in iter(int, 1)), budget_s)
+            scale = 1e9 if unit == "GB/s" else 1e12
+            out[name] = {"value": round(done / dt / scale, 6), "unit": unit, "seconds": round(dt, 2),
+                         "calls": calls, "us_per_call": round(dt / calls * 1e6, 1), "cores": 1, "kind": "oracle",
+                         "sample": f"the whole {name} batch per call, fp64"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -473,6 +615,8 @@ def main():
                                            "sparse_decode_bf16,sparse_decode_fp8,single_decode_bf16,decode_int8",
                     help="comma list of workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget-secondary", type=float, default=3.0,
+                    help="seconds of oracle work for each secondary workload's and each single-thread cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as captured HIP graphs (plan + stores, then the attention calls) "
@@ -520,21 +664,18 @@ def main():
                                          workloads, graph=graph)
             secondary[name] = {"value": round(v2, 2), "unit": UNITS[name], "ms_per_step": round(ms2, 4),
                                "config": r2.describe(), "roofline": roof2}
+            if not args.no_cpu_baseline:
+                secondary[name]["cpu_baseline"] = cpu_baseline_of(r2, args.cpu_budget_secondary)
             del r2
         except Exception as e:  # a workload whose kernel is missing is reported, not hidden
             secondary[name] = {"error": f"{type(e).__name__}: {e}"}
         torch.cuda.empty_cache()
     if secondary:
         line["secondary"] = secondary
-    if not args.no_cpu_baseline and hasattr(runner, "cpu_baseline"):
-        import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:
-            cores = 1
-        cb = runner.cpu_baseline(args.cpu_budget, oracle)
-        cb.update({"cores": cores, "kind": "oracle"})
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline_of(runner, args.cpu_budget)
+        if args.workload == "decode_bf16":
+            cb["single_thread"] = single_thread_baselines(runner, args.cpu_budget_secondary)
         line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 

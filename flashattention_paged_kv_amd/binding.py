@@ -16,7 +16,9 @@ from dataclasses import dataclass
 from typing import Optional, Tuple
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpkv.so")
+# the in-tree build; PKV_LIBRARY names another build of the same library (the
+# host-AddressSanitizer build of the ABI tests)
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(PKG, "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
 PKV_BF16, PKV_FP8_E4M3, PKV_SAGE_INT8 = 0, 1, 2
