@@ -154,6 +154,56 @@ def ingest_counters(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_c
     print(json.dumps(out))
 
 
+SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
+SQ_ENGINES = 32  # the SQ cycle counters add up over 32 shader engines (8 XCDs x 4)
+
+
+def summarize_sq_counters(workload, csv_paths, commands):
+    """Per-dispatch averages of the SQ counters in rocprofv3 --pmc CSV files for
+    the workload's main kernel, with derived utilisations, written to
+    profiles/<kernel>.sq_counters.<workload>.txt."""
+    import collections
+    import csv
+    kernel = CALL_KERNELS[workload][0]
+    avg = {}
+    dispatches = 0
+    for path in csv_paths:
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel in r["Kernel_Name"]:
+                    per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        if not per:
+            raise SystemExit(f"no dispatch of {kernel} in {path}")
+        dispatches = len(per)
+        for name in {k for v in per.values() for k in v}:
+            avg[name] = sum(v.get(name, 0.0) for v in per.values()) / len(per)
+    lines = [f"SQ counters of {kernel}, workload {workload} ({dispatches} dispatches averaged per pass)",
+             f"source sha {source_hash(workload)}", "", "commands:"] + [f"  {c}" for c in commands] + ["", "per dispatch:"]
+    lines += [f"  {k:32s} {v:14.6g}" for k, v in sorted(avg.items())]
+    cyc = avg.get("SQ_CYCLES", 0.0) / SQ_ENGINES  # kernel cycles
+    if cyc > 0:
+        lines += ["", "derived (kernel cycles = SQ_CYCLES / 32 shader engines; per SIMD = / 1024 SIMDs):",
+                  f"  kernel cycles                          {cyc:14.6g}"]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            lines.append(f"  matrix cores busy (share of SIMD time)  {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / SIMDS / cyc:14.3f}")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg and avg.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            lines.append(f"  MFMA busy cycles with VALU co-issue     "
+                         f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:14.3f}")
+        if "SQ_INSTS_VALU" in avg:
+            lines.append(f"  VALU instructions per SIMD cycle        {avg['SQ_INSTS_VALU'] / SIMDS / cyc:14.4f}")
+        if "SQ_INSTS_VALU_TRANS_F32" in avg and "SQ_INSTS_MFMA" in avg:
+            lines.append(f"  VALU instructions per MFMA              {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:14.2f}")
+            lines.append(f"  transcendental instructions per MFMA    "
+                         f"{avg['SQ_INSTS_VALU_TRANS_F32'] / avg['SQ_INSTS_MFMA']:14.2f}")
+    if avg.get("SQ_INSTS_LDS"):
+        lines.append(f"  LDS bank-conflict cycles per LDS instr  {avg.get('SQ_LDS_BANK_CONFLICT', 0.0) / avg['SQ_INSTS_LDS']:14.3f}")
+    path = os.path.join(PROFILES, f"{kernel}.sq_counters.{workload}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def copy_calibration():
     """A plain streaming kernel of known size: 1 GiB read once, 1 GiB written once."""
     import torch
@@ -627,7 +677,13 @@ def main():
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV files (host only)")
     ap.add_argument("--commands", default="", help="with --ingest-counters: the profiler commands, ' ;; '-separated")
+    ap.add_argument("--summarize-sq-counters", nargs="+", metavar="CSV",
+                    help="write profiles/<kernel>.sq_counters.<workload>.txt from rocprofv3 --pmc CSV files (host only)")
     args = ap.parse_args()
+    if args.summarize_sq_counters:
+        summarize_sq_counters(args.workload, args.summarize_sq_counters,
+                              [c.strip() for c in args.commands.split(";;") if c.strip()])
+        return
     if args.ingest_counters:
         ingest_counters(args.workload, *args.ingest_counters,
                         commands=[c.strip() for c in args.commands.split(";;") if c.strip()])

@@ -64,10 +64,25 @@ struct Smem8 {
   static constexpr int TOTAL = SFK0 + kSlotStages8 * SFK_BYTES;
 };
 
-// 16-byte chunk c of key row r sits at chunk position c ^ (r % 8): the K
-// reads (32 keys, one chunk column) and the transposing V reads (8 rows,
-// one chunk column) spread over the banks.
-__device__ __forceinline__ int swz8(int row) { return row & 7; }
+// 16-byte chunk c of key row r sits at chunk position c ^ swz8(r).  Two
+// 128-byte rows share one 256-byte line of the LDS banks, so a row's bank
+// group is its chunk position plus 8 for odd rows.  The mask takes bits 1..3
+// of r, permuted (bit 1 -> bit 0, bit 2 -> bit 1, bit 3 -> bit 2), XOR the
+// row's parity:
+//  * K reads (16 consecutive rows, one chunk column, per 16 lanes): the even
+//    rows take 8 distinct positions and so do the odd ones, so the 16 rows
+//    cover the 16 bank groups;
+//  * transposing V reads (rows {0..3, 8..11} or {4..7, 12..15} of a 16-key
+//    window, one chunk column per 16 lanes, columns c and c + 1 side by side
+//    in 32 lanes): the masks of a row set differ in bits 1..2 within each
+//    parity and in bit 0 across parities, so the positions are distinct
+//    within 16 lanes and within 32 lanes.
+// The mask depends on r % 16 only, so rows 16, 32, ... further take the same
+// per-lane offsets plus an immediate.
+__device__ __forceinline__ int swz8(int row) {
+  const int h = row >> 1;
+  return (((h & 1) << 1) | (h & 4) | ((h >> 1) & 1)) ^ (row & 1);
+}
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
