@@ -57,9 +57,15 @@ constexpr int kSlotStages = 3;  // req_to_token entries are requested 2 tiles ah
 // XOR-swizzled against bank conflicts:
 //  * K: chunk c of key r at position c ^ (r % CH) -- the 16-byte row reads of
 //    the Sᵀ product touch one chunk of many consecutive keys;
-//  * V: chunk c of key r at position c ^ (2 (r % 8) % CH) -- each transpose
-//    read touches a 32-byte chunk pair of 4 consecutive keys, and XOR with an
-//    even value keeps pairs aligned while moving each key to another pair.
+//  * V: chunk c of key r at position c ^ swz_v(r).  A transposing read of a
+//    16-lane group touches the 32-byte chunk pair (c, c + 1) of 4
+//    consecutive keys, and the two groups of 32 lanes read the pairs c and
+//    c + 2 of the same keys, i.e. the aligned quad of chunks 4 (c / 4) ..
+//    +3.  For head_dim 128 (256-byte rows, one row per line of the 64 banks)
+//    swz_v(r) = 4 (r % 4) + 2 ((r / 4) % 2) sends the 4 keys' quads to 4
+//    different quads, so 32 lanes read 16 distinct 16-byte bank groups; an
+//    even mask keeps the pairs aligned.  For head_dim 64 the mask is
+//    2 (r % 8) % 8.
 template <int D>
 struct ExtSmem {
   static constexpr int RB = D * 2;                        // bytes per key row
@@ -76,7 +82,9 @@ struct ExtSmem {
 template <int D>
 __device__ __forceinline__ int swz_k(int row) { return row & (ExtSmem<D>::CH - 1); }
 template <int D>
-__device__ __forceinline__ int swz_v(int row) { return (2 * (row & 7)) & (ExtSmem<D>::CH - 1); }
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) + 2 * ((row >> 2) & 1) : (2 * (row & 7)) & (ExtSmem<D>::CH - 1);
+}
 template <int D>
 __device__ __forceinline__ int k_off(int row, int chunk) {
   return row * ExtSmem<D>::RB + ((chunk ^ swz_k<D>(row)) << 4);
