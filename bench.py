@@ -204,6 +204,54 @@ def summarize_sq_counters(workload, csv_paths, commands):
     print("\n".join(lines))
 
 
+def summarize_trace(workload, stats_csv, bench_log, command):
+    """profiles/<kernel>.<workload>.txt from a rocprofv3 --kernel-trace --stats
+    run of bench.py: the library kernels' call counts and durations, and the
+    bench line of the same run."""
+    import csv
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"]
+            if "pkv::" not in name:
+                continue  # torch's own set-up kernels
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda t: -t[1] * t[2])
+    with open(bench_log) as f:
+        line = json.loads([x for x in f if x.startswith("{")][-1])
+    roof = line["roofline"]
+    call = [t for t in rows if any(k in t[0] for k in CALL_KERNELS[workload])]
+    kernel = CALL_KERNELS[workload][0]
+    out = [f"# rocprofv3 kernel trace: {kernel} on the {workload} workload", "",
+           "Command (repo root on one MI355X; TMPDIR=/tmp):", f"  {command}", "",
+           "Library kernels (from the kernel_stats.csv of that run; torch set-up kernels omitted):", "",
+           f"  {'kernel':58s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} {'share':>7s}"]
+    for name, calls, avg, mn, mx, pct in rows:
+        short = name.split("(")[0]
+        out.append(f"  {short[:58]:58s} {calls:6d} {avg:9.2f} {mn:9.2f} {mx:9.2f} {pct:6.1f}%")
+    total = 0.0
+    seen = set()
+    for k in CALL_KERNELS[workload]:
+        for name, calls, avg, *_ in call:
+            if k in name and name not in seen:
+                seen.add(name)
+                total += avg
+    unit = roof["unit"]
+    work = roof.get("algorithmic_bytes_per_launch") or roof.get("algorithmic_flops_per_launch")
+    out += ["", f"One attention call = {' + '.join(CALL_KERNELS[workload])}: sum of averages {total:.2f} us.",
+            f"The same run's bench line (HIP events around the attention block, per call): avg_launch_us "
+            f"{roof['avg_launch_us']}, achieved {roof['achieved']} {unit} = {100 * roof['frac']:.1f}% of "
+            f"{roof['peak']} {unit}.",
+            f"Algorithmic work per call: {work} " + ("bytes (K+V read)" if unit == "GB/s" else "flops (4*d*Hq per unmasked pair)"),
+            f"Step time in that run: {line['ms_per_step']} ms ({line['config'].get('layers_per_step')} layers/step).",
+            f"Kernel sources sha {source_hash(workload)}."]
+    path = os.path.join(PROFILES, f"{kernel}.{workload}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def copy_calibration():
     """A plain streaming kernel of known size: 1 GiB read once, 1 GiB written once."""
     import torch
@@ -677,9 +725,14 @@ def main():
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV files (host only)")
     ap.add_argument("--commands", default="", help="with --ingest-counters: the profiler commands, ' ;; '-separated")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
+                    help="write profiles/<kernel>.<workload>.txt from a rocprofv3 --kernel-trace --stats run (host only)")
     ap.add_argument("--summarize-sq-counters", nargs="+", metavar="CSV",
                     help="write profiles/<kernel>.sq_counters.<workload>.txt from rocprofv3 --pmc CSV files (host only)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.workload, *args.summarize_trace, command=args.commands)
+        return
     if args.summarize_sq_counters:
         summarize_sq_counters(args.workload, args.summarize_sq_counters,
                               [c.strip() for c in args.commands.split(";;") if c.strip()])
