@@ -16,6 +16,8 @@
 //  * PV is Oᵀ = Vᵀ·Pᵀ with Vᵀ as the A operand: each lane loads 8 V rows
 //    (16 bytes of each) and transposes them to operands with byte permutes,
 //    so no LDS round trip is needed.
+// K and V rows are read once; with few kv heads per token the loads carry
+// the non-temporal hint (STREAM).
 //
 // Items with one split write bf16 O and lse directly; otherwise the split's
 // normalised partial O and log2-sum-exp go to scratch and the merge kernel
@@ -46,7 +48,7 @@ __device__ __forceinline__ uint32_t tile_slot(const int32_t* __restrict__ rtt_ro
   return clamp_slot_u32(rtt_row[tok], last);
 }
 
-template <int D>
+template <int D, bool STREAM>
 __device__ __forceinline__ void load_tile(KVTile<D>& t, uint32_t slot, const uint16_t* __restrict__ kbase,
                                           const uint16_t* __restrict__ vbase, uint32_t row_elems, int lane) {
   constexpr int KB = D / 32;
@@ -56,8 +58,8 @@ __device__ __forceinline__ void load_tile(KVTile<D>& t, uint32_t slot, const uin
   const uint16_t* k1 = kbase + row_offset(sk1, row_elems) + 8 * j;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    t.k[0][kb] = ldg16(k0 + 32 * kb);
-    t.k[1][kb] = ldg16(k1 + 32 * kb);
+    t.k[0][kb] = ldg16_once<STREAM>(k0 + 32 * kb);
+    t.k[1][kb] = ldg16_once<STREAM>(k1 + 32 * kb);
   }
   // d = 64: lanes 8..15 re-read columns of their own row; they only feed
   // output rows d >= 64, which are never stored
@@ -66,7 +68,7 @@ __device__ __forceinline__ void load_tile(KVTile<D>& t, uint32_t slot, const uin
   for (int r = 0; r < 8; ++r) {
     const int tau = r < 4 ? 4 * j + r : 16 + 4 * j + (r - 4);
     const uint32_t sv = __shfl(slot, tau);
-    t.v[r] = ldg16(vbase + row_offset(sv, row_elems) + dcol);
+    t.v[r] = ldg16_once<STREAM>(vbase + row_offset(sv, row_elems) + dcol);
   }
 }
 
@@ -185,7 +187,7 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int p
 // before them, whichever segments the three tiles belong to.  Two register
 // buffers are used in turn.  When the computed tile enters a new segment the
 // previous one is written out and the online-softmax state restarts.
-template <int D>
+template <int D, bool STREAM>
 __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int s0, int s1, int unit, int4* win_rec,
                                              int2* win_req) {
   const int g = unit / a.head_groups, hg = unit - g * a.head_groups;
@@ -221,7 +223,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int s0, int s1
 
   auto rtt_of = [&](const TileCursor& c) { return a.rtt + (int64_t)c.row * a.rtt_stride; };
   KVTile<D> ta, tb;
-  load_tile<D>(ta, tile_slot(rtt_of(C), C.t0, C.kv_end, last, lane), kbase, vbase, row_elems, lane);
+  load_tile<D, STREAM>(ta, tile_slot(rtt_of(C), C.t0, C.kv_end, last, lane), kbase, vbase, row_elems, lane);
   TileCursor L = next_tile<kDecodeTile>(a, w, C, s1, lane);
   uint32_t s_odd = tile_slot(rtt_of(L), L.t0, L.kv_end, last, lane), s_even;
   TileCursor S = next_tile<kDecodeTile>(a, w, L, s1, lane);
@@ -247,12 +249,12 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int s0, int s1
 
   for (;;) {
     s_even = tile_slot(rtt_of(S), S.t0, S.kv_end, last, lane);
-    load_tile<D>(tb, s_odd, kbase, vbase, row_elems, lane);
+    load_tile<D, STREAM>(tb, s_odd, kbase, vbase, row_elems, lane);
     __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
     compute_tile<D>(ta, qop, C.t0, min(C.kv_end, C.lim + qi + 1), a.scale_log2, m, lpart, acc, lane);
     if (!advance()) break;
     s_odd = tile_slot(rtt_of(S), S.t0, S.kv_end, last, lane);
-    load_tile<D>(ta, s_even, kbase, vbase, row_elems, lane);
+    load_tile<D, STREAM>(ta, s_even, kbase, vbase, row_elems, lane);
     __builtin_amdgcn_sched_barrier(0);
     compute_tile<D>(tb, qop, C.t0, min(C.kv_end, C.lim + qi + 1), a.scale_log2, m, lpart, acc, lane);
     if (!advance()) break;
@@ -263,7 +265,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int s0, int s1
 // the same chunk, so the rows of one token are requested together.  The plan
 // lays the requests' tiles end to end and cuts them into chunks of equal
 // length; a chunk is a list of request segments.
-template <int D, int WPB>
+template <int D, int WPB, bool STREAM>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(DecodeArgs a) {
   const int32_t* __restrict__ ws = a.ws;
   // 1-D grid, unit group fastest: the workgroups of one chunk are
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
   const int s0 = tab ? ws[tab + c] : c, s1 = tab ? ws[tab + c + 1] : c + 1;
   __shared__ int4 win_rec[WPB][64];
   __shared__ int2 win_req[WPB][64];
-  decode_chunk<D>(a, s0, s1, unit, win_rec[wv], win_req[wv]);
+  decode_chunk<D, STREAM>(a, s0, s1, unit, win_rec[wv], win_req[wv]);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
@@ -299,22 +301,28 @@ hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int64_t capaci
   return hipGetLastError();
 }
 
+// Kernel instance for head_dim D, wpb waves per workgroup and the load
+// form; fewer than 8 units always stream (decode_streams).
+template <int D>
+const void* decode_bf16_kernel_for(int wpb, bool stream) {
+  if (wpb == 8) return stream ? (const void*)decode_bf16_kernel<D, 8, true> : (const void*)decode_bf16_kernel<D, 8, false>;
+  return wpb == 4 ? (const void*)decode_bf16_kernel<D, 4, true> : wpb == 2 ? (const void*)decode_bf16_kernel<D, 2, true>
+                                                                            : (const void*)decode_bf16_kernel<D, 1, true>;
+}
+
 hipError_t launch_decode_bf16(const DecodeArgs& a, int head_dim, int64_t capacity, int32_t batch,
                               hipStream_t s) {
   if (capacity <= 0 || batch <= 0) return hipSuccess;
   // up to 8 waves per workgroup: the kv heads of one split run side by side
   const int units = a.hkv * a.head_groups;
   const int wpb = decode_waves_per_block(units);
-  dim3 grid((unsigned)(capacity * ceil_div(units, wpb)));
-  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * wpb), 0, s, a); };
-  if (head_dim == 128) {
-    if (wpb == 8) go(decode_bf16_kernel<128, 8>); else if (wpb == 4) go(decode_bf16_kernel<128, 4>);
-    else if (wpb == 2) go(decode_bf16_kernel<128, 2>); else go(decode_bf16_kernel<128, 1>);
-  } else {
-    if (wpb == 8) go(decode_bf16_kernel<64, 8>); else if (wpb == 4) go(decode_bf16_kernel<64, 4>);
-    else if (wpb == 2) go(decode_bf16_kernel<64, 2>); else go(decode_bf16_kernel<64, 1>);
-  }
-  return hipGetLastError();
+  const bool stream = decode_streams(units);
+  const void* k = head_dim == 128 ? decode_bf16_kernel_for<128>(wpb, stream) : decode_bf16_kernel_for<64>(wpb, stream);
+  DecodeArgs args = a;
+  void* kargs[] = {&args};
+  const hipError_t e = hipLaunchKernel(k, dim3((unsigned)(capacity * ceil_div(units, wpb))), dim3(64 * wpb), kargs, 0, s);
+  const hipError_t last = hipGetLastError();  // also clears what the launch left
+  return e != hipSuccess ? e : last;
 }
 
 hipError_t resident_items_of(const void* kernel, int wpb, int units, int64_t* items) {
@@ -330,13 +338,8 @@ hipError_t resident_items_of(const void* kernel, int wpb, int units, int64_t* it
 
 hipError_t decode_bf16_resident_items(int head_dim, int units, int64_t* items) {
   const int wpb = decode_waves_per_block(units);
-  const void* k = nullptr;
-  if (head_dim == 128)
-    k = wpb == 8 ? (const void*)decode_bf16_kernel<128, 8> : wpb == 4 ? (const void*)decode_bf16_kernel<128, 4>
-      : wpb == 2 ? (const void*)decode_bf16_kernel<128, 2> : (const void*)decode_bf16_kernel<128, 1>;
-  else
-    k = wpb == 8 ? (const void*)decode_bf16_kernel<64, 8> : wpb == 4 ? (const void*)decode_bf16_kernel<64, 4>
-      : wpb == 2 ? (const void*)decode_bf16_kernel<64, 2> : (const void*)decode_bf16_kernel<64, 1>;
+  const bool stream = decode_streams(units);
+  const void* k = head_dim == 128 ? decode_bf16_kernel_for<128>(wpb, stream) : decode_bf16_kernel_for<64>(wpb, stream);
   return resident_items_of(k, wpb, units, items);
 }
 

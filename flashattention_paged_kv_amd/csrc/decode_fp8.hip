@@ -74,6 +74,7 @@ __device__ __forceinline__ uint32_t slot_at(const int32_t* __restrict__ rtt_row,
   return clamp_slot_u32(rtt_row[min(t0 + lane, kv_end - 1)], last);
 }
 
+template <bool STREAM>
 __device__ __forceinline__ void load_tile8(Tile8& t, uint32_t slot, int t0, int kv_end,
                                            const float* __restrict__ sfk_row, int k_block,
                                            const uint8_t* __restrict__ kbase, const uint8_t* __restrict__ vbase,
@@ -85,13 +86,13 @@ __device__ __forceinline__ void load_tile8(Tile8& t, uint32_t slot, int t0, int 
   for (int blk = 0; blk < 4; ++blk) {
     const uint32_t sk = __shfl(slot, 16 * blk + l16);
     const uint8_t* p = kbase + row_offset(sk, row_bytes) + 32 * j;
-    t.k[blk][0] = ldg16(p);
-    t.k[blk][1] = ldg16(p + 16);
+    t.k[blk][0] = ldg16_once<STREAM>(p);
+    t.k[blk][1] = ldg16_once<STREAM>(p + 16);
   }
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const uint32_t sv = __shfl(slot, tok_of(j, e));
-    t.v[e] = ldg8(vbase + row_offset(sv, row_bytes) + 8 * l16);
+    t.v[e] = ldg8_once<STREAM>(vbase + row_offset(sv, row_bytes) + 8 * l16);
   }
 }
 
@@ -199,7 +200,7 @@ __device__ __forceinline__ void finish_empty8(const DecodeArgs& a, SegWindow& w,
 // tiles belong to.
 // MULTI: several new tokens per request (per-lane causal limits); the
 // one-token instance keeps none of that state in the tile loop.
-template <bool MULTI, bool I8>
+template <bool MULTI, bool I8, bool STREAM>
 __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, int s1, int unit, int4* win_rec,
                                                  int2* win_req) {
   constexpr int D = 128;
@@ -298,7 +299,7 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
   auto rtt_of = [&](const TileCursor& c) { return a.rtt + (int64_t)c.row * a.rtt_stride; };
   auto sfk_of = [&](const TileCursor& c) { return a.sfk + ((int64_t)c.b * a.hkv + g) * a.sfk_stride; };
   Tile8 ta, tb;
-  load_tile8(ta, slot_at(rtt_of(C), C.t0, C.kv_end, last, lane), C.t0, C.kv_end, sfk_of(C), a.k_block, kbase, vbase,
+  load_tile8<STREAM>(ta, slot_at(rtt_of(C), C.t0, C.kv_end, last, lane), C.t0, C.kv_end, sfk_of(C), a.k_block, kbase, vbase,
              row_bytes, lane);
   TileCursor L = next_tile<kTile8>(a, w, C, s1, lane);
   uint32_t s_odd = slot_at(rtt_of(L), L.t0, L.kv_end, last, lane), s_even;
@@ -325,12 +326,12 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
 
   for (;;) {
     s_even = slot_at(rtt_of(S), S.t0, S.kv_end, last, lane);
-    load_tile8(tb, s_odd, L.t0, L.kv_end, sfk_of(L), a.k_block, kbase, vbase, row_bytes, lane);
+    load_tile8<STREAM>(tb, s_odd, L.t0, L.kv_end, sfk_of(L), a.k_block, kbase, vbase, row_bytes, lane);
     __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of this tile's math
     compute(ta, C.t0, MULTI ? min(C.kv_end, C.lim + qi + 1) : C.kv_end);
     if (!advance()) break;
     s_odd = slot_at(rtt_of(S), S.t0, S.kv_end, last, lane);
-    load_tile8(ta, s_even, L.t0, L.kv_end, sfk_of(L), a.k_block, kbase, vbase, row_bytes, lane);
+    load_tile8<STREAM>(ta, s_even, L.t0, L.kv_end, sfk_of(L), a.k_block, kbase, vbase, row_bytes, lane);
     __builtin_amdgcn_sched_barrier(0);
     compute(tb, C.t0, MULTI ? min(C.kv_end, C.lim + qi + 1) : C.kv_end);
     if (!advance()) break;
@@ -338,7 +339,7 @@ __device__ __forceinline__ void decode_fp8_chunk(const DecodeArgs& a, int s0, in
 }
 
 // WPB units of one chunk per workgroup, as in the bf16 decode.
-template <int WPB, bool MULTI, bool I8>
+template <int WPB, bool MULTI, bool I8, bool STREAM>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) void decode_fp8_kernel(DecodeArgs a) {
   const int32_t* __restrict__ ws = a.ws;
   // 1-D grid, unit group fastest: the workgroups of one chunk are
@@ -353,16 +354,22 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2))) v
   const int s0 = tab ? ws[tab + c] : c, s1 = tab ? ws[tab + c + 1] : c + 1;
   __shared__ int4 win_rec[WPB][64];
   __shared__ int2 win_req[WPB][64];
-  decode_fp8_chunk<MULTI, I8>(a, s0, s1, unit, win_rec[wv], win_req[wv]);
+  decode_fp8_chunk<MULTI, I8, STREAM>(a, s0, s1, unit, win_rec[wv], win_req[wv]);
 }
 
+// Kernel instance for wpb waves per workgroup and the load form; fewer than
+// 8 units always stream (decode_streams).
 template <bool MULTI, bool I8>
-void launch_decode_fp8_as(const DecodeArgs& a, dim3 grid, int wpb, hipStream_t s) {
-  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * wpb), 0, s, a); };
-  if (wpb == 8) go(decode_fp8_kernel<8, MULTI, I8>);
-  else if (wpb == 4) go(decode_fp8_kernel<4, MULTI, I8>);
-  else if (wpb == 2) go(decode_fp8_kernel<2, MULTI, I8>);
-  else go(decode_fp8_kernel<1, MULTI, I8>);
+const void* decode_fp8_kernel_for(int wpb, bool stream) {
+  if (wpb == 8)
+    return stream ? (const void*)decode_fp8_kernel<8, MULTI, I8, true> : (const void*)decode_fp8_kernel<8, MULTI, I8, false>;
+  return wpb == 4 ? (const void*)decode_fp8_kernel<4, MULTI, I8, true>
+       : wpb == 2 ? (const void*)decode_fp8_kernel<2, MULTI, I8, true> : (const void*)decode_fp8_kernel<1, MULTI, I8, true>;
+}
+
+static const void* decode_fp8_kernel_of(bool multi, bool qk_int8, int wpb, bool stream) {
+  if (multi) return qk_int8 ? decode_fp8_kernel_for<true, true>(wpb, stream) : decode_fp8_kernel_for<true, false>(wpb, stream);
+  return qk_int8 ? decode_fp8_kernel_for<false, true>(wpb, stream) : decode_fp8_kernel_for<false, false>(wpb, stream);
 }
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool qk_int8, int64_t capacity, int32_t batch, hipStream_t s) {
@@ -370,27 +377,17 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool qk_int8, int64_t capacity
   if (capacity <= 0 || batch <= 0) return hipSuccess;
   const int units = a.hkv * a.head_groups;
   const int wpb = decode_waves_per_block(units);
-  const dim3 grid((unsigned)(capacity * ceil_div(units, wpb)));
-  if (a.q_len > 1) {
-    if (qk_int8) launch_decode_fp8_as<true, true>(a, grid, wpb, s);
-    else launch_decode_fp8_as<true, false>(a, grid, wpb, s);
-  } else {
-    if (qk_int8) launch_decode_fp8_as<false, true>(a, grid, wpb, s);
-    else launch_decode_fp8_as<false, false>(a, grid, wpb, s);
-  }
-  return hipGetLastError();
-}
-
-template <bool I8>
-const void* decode_fp8_kernel_for(int wpb) {
-  return wpb == 8 ? (const void*)decode_fp8_kernel<8, false, I8> : wpb == 4 ? (const void*)decode_fp8_kernel<4, false, I8>
-       : wpb == 2 ? (const void*)decode_fp8_kernel<2, false, I8> : (const void*)decode_fp8_kernel<1, false, I8>;
+  const void* k = decode_fp8_kernel_of(a.q_len > 1, qk_int8, wpb, decode_streams(units));
+  DecodeArgs args = a;
+  void* kargs[] = {&args};
+  const hipError_t e = hipLaunchKernel(k, dim3((unsigned)(capacity * ceil_div(units, wpb))), dim3(64 * wpb), kargs, 0, s);
+  const hipError_t last = hipGetLastError();  // also clears what the launch left
+  return e != hipSuccess ? e : last;
 }
 
 hipError_t decode_fp8_resident_items(int units, bool qk_int8, int64_t* items) {
   const int wpb = decode_waves_per_block(units);
-  return resident_items_of(qk_int8 ? decode_fp8_kernel_for<true>(wpb) : decode_fp8_kernel_for<false>(wpb), wpb, units,
-                           items);
+  return resident_items_of(decode_fp8_kernel_of(false, qk_int8, wpb, decode_streams(units)), wpb, units, items);
 }
 
 }  // namespace pkv

@@ -31,6 +31,22 @@ __device__ __forceinline__ int opaque(int x) {
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ldg8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// Loads of data read once (the decode's K/V rows), with the non-temporal
+// hint (global_load ... nt) when STREAM is set: such lines are not kept in
+// the caches.  Whether that pays depends on the layout read (the decode
+// launchers choose per launch).
+template <bool STREAM>
+__device__ __forceinline__ u32x4 ldg16_once(const void* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return ldg16(p);
+}
+template <bool STREAM>
+__device__ __forceinline__ u32x2 ldg8_once(const void* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  else return ldg8(p);
+}
+
 __device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -237,6 +237,12 @@ hipError_t decode_fp8_resident_items(int units, bool qk_int8, int64_t* items);
 hipError_t resident_items_of(const void* kernel, int wpb, int units, int64_t* items);
 // Waves per workgroup the decode launchers use for `units` waves per item.
 inline int decode_waves_per_block(int units) { return units >= 8 ? 8 : (units >= 4 ? 4 : (units >= 2 ? 2 : 1)); }
+// The decode kernels read K/V with non-temporal loads when at most two
+// workgroups cover the kv heads of a token (up to 16 (kv head, head group)
+// units).  Measured on MI355X: 7-12% faster split kernels for 8 and 16 kv
+// heads; with 40 kv heads (five workgroups per token) the same loads gained
+// nothing on the dense decode and lost 5% on the 8-bit block-sparse one.
+inline bool decode_streams(int units) { return units <= 2 * decode_waves_per_block(units); }
 hipError_t launch_extend_bf16(const ExtendArgs& a, int head_dim, int64_t capacity, hipStream_t s);
 
 }  // namespace pkv
