@@ -75,8 +75,11 @@ def test_medium_decode_ragged(seed, kv_chunk):
     assert_lse_close(lse, rlse, "medium decode")
 
 
+# (24, 24, 64) and (48, 24, 128) have 24 (kv head, head group) units per
+# token: the kernel instances with plain (not non-temporal) K/V loads
 @pytest.mark.parametrize("hq,hkv,d,page", [(8, 8, 128, 1), (64, 8, 128, 64), (40, 2, 128, 16),
-                                           (16, 4, 64, 16), (12, 4, 64, 2), (32, 8, 64, 256)])
+                                           (16, 4, 64, 16), (12, 4, 64, 2), (32, 8, 64, 256),
+                                           (24, 24, 64, 16), (48, 24, 128, 16)])
 def test_head_layouts_and_pages(hq, hkv, d, page):
     spec = Spec("dec_shape", "decode", 5, hq, hkv, d, page, (0, 700), 1)
     hb = make_host_batch(spec, 3)

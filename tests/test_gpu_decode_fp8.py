@@ -209,8 +209,11 @@ def run_fp8_multi(hb, n, v_mean=None, kv_chunk=0, seed=None):
     return host(out), lse.cpu().numpy().astype(np.float64), sfq_rows
 
 
+# (5, 64, 8): 40 columns per kv head, three head groups, 24 units: the
+# multi-token instance with plain K/V loads
 @pytest.mark.parametrize("n,hq,hkv,kv_chunk,with_vm", [(2, 32, 8, 0, False), (4, 32, 8, 0, True), (8, 8, 8, 0, False),
-                                                     (3, 16, 2, 128, True), (16, 8, 1, 0, False), (5, 40, 8, 64, False)])
+                                                     (3, 16, 2, 128, True), (16, 8, 1, 0, False), (5, 40, 8, 64, False),
+                                                     (5, 64, 8, 0, False)])
 def test_fp8_several_new_tokens_per_request(n, hq, hkv, kv_chunk, with_vm):
     """n new tokens per request checked in one 8-bit decode call: new token i
     sees keys 0 .. L - n + i, one sfQ per new-token row; the oracle is the
@@ -224,6 +227,19 @@ def test_fp8_several_new_tokens_per_request(n, hq, hkv, kv_chunk, with_vm):
                                 lay.cu_seqlens_q, sfq_rows, hb.sfk, hb.sfv, spec.k_block, v_mean=vm)
     check_rel_l2(o, ro, f"decode E4M3 n={n}")
     assert np.abs(l - rl).max() <= 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "int8"])
+def test_8bit_decode_many_kv_heads(dtype):
+    """24 kv heads of one query head each (24 units per token): the kernel
+    instances with plain K/V loads, against the Sage oracle."""
+    spec = Spec("f8_mha", "decode", 5, 24, 24, 128, 16, (0, 800), 1, dtype=dtype, k_block=64)
+    hb = make_host_batch(spec, 31)
+    o, lse = run_fp8(hb, split_target=48)
+    ro, rlse = oracle_fp8(hb)
+    check_rel_l2(o, ro, f"decode {dtype} 24 kv heads")
+    assert np.abs(lse - rlse)[np.isfinite(rlse)].max() <= 1e-3
+    assert np.array_equal(np.isfinite(lse), np.isfinite(rlse))
 
 
 # two to eight keys per request: few keys, so each request's E4M3 rounding of
