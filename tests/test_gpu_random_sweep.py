@@ -2,6 +2,8 @@
 grouping, head_dim, page size, lengths with empty and tiny requests, block
 masks), every case against the fp64 oracle.  They complement the hand-picked
 cases with combinations nobody chose; a failure prints the case."""
+import os
+
 import numpy as np
 import pytest
 
@@ -11,11 +13,12 @@ from workloads import Spec, make_host_batch
 
 pytestmark = pytest.mark.gpu
 
-CASES = 16
+# cases per family; PKV_SWEEP_CASES raises it for a longer run
+CASES = int(os.environ.get("PKV_SWEEP_CASES", "16"))
 
 
 def _draw_shape(rng, d_choices=(64, 128), max_group=16, max_hkv=8, max_batch=9):
-    hkv = int(rng.choice([h for h in (1, 2, 3, 4, 8) if h <= max_hkv]))
+    hkv = int(rng.choice([h for h in (1, 2, 3, 4, 8, 12, 24) if h <= max_hkv]))
     group = int(rng.choice([g for g in (1, 2, 3, 4, 5, 8, 16) if g <= max_group]))
     d = int(rng.choice(d_choices))
     page = int(rng.choice([1, 2, 16, 64]))
@@ -36,7 +39,9 @@ def test_random_bf16_decode():
     from test_gpu_decode import oracle_decode, run_decode
     rng = np.random.default_rng(2024)
     for case in range(CASES):
-        B, hq, hkv, d, page = _draw_shape(rng)
+        # up to 24 kv heads: layouts with more than 16 units per token take
+        # the kernel instances with plain K/V loads
+        B, hq, hkv, d, page = _draw_shape(rng, max_group=8, max_hkv=24)
         q_len = int(rng.choice([1, 1, 2, 4]))
         spec = Spec(f"rd{case}", "decode", B, hq, hkv, d, page, _lengths(rng, B, 0, 900), q_len)
         hb = make_host_batch(spec, case)
